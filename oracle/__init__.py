@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for the dropless MoE layer.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchmark's CPU
+baseline, never by the GPU library.  It shares no code with the GPU path; the only thing both
+sides see is the seeded input arrays from the ``workloads`` package.
+
+Every function is pinned by CPU tests against properties the pages and the mathematics fix
+(library sort routines, dense-MLP closed forms, finite differences, conservation identities);
+the pages themselves print no worked values.
+"""
+from .formats import bf16_to_f64, e4m3_to_f64, dequant_rows_1x128, dequant_blocks_128x128
+from .moe_ref import (route, plan, Plan, forward, backward, token_forward, token_backward,
+                      weight_grad_entries, d_logits_from_dw)
+
+__all__ = ["bf16_to_f64", "e4m3_to_f64", "dequant_rows_1x128", "dequant_blocks_128x128", "route",
+           "plan", "Plan", "forward", "backward", "token_forward", "token_backward",
+           "weight_grad_entries", "d_logits_from_dw"]

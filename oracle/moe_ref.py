@@ -1,0 +1,266 @@
+"""Plain fp64 CPU oracle of the dropless MoE layer, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
+use this module; the GPU library never imports or calls it, and it shares no code with the GPU
+path.  It is written for clarity, not speed: one Python loop over experts, the shape of the
+per-expert Python-loop baseline described on the TE page (below), with numpy matmuls in fp64.
+
+Pages cited (title as published; section headings translated in brackets):
+  [Prime]  "Prime Mega MoE: tanításra is jó a DeepSeek MoE kernele" (neuraldaily.news)
+  [JAX]    "Az NVIDIA szerint tízszer gyorsabb lett a dropless MoE tanítása JAX-ban" (aihirek.info)
+  [TE]     "NVIDIA מציגה דרך יעילה לאמן מודלי MoE בביולוגיה" (sitech.ge)
+  [Mega]   the DeepGEMM "Mega MoE" announcement on itsolotime.com (Thai)
+
+What is computed, and where the pages state it:
+  route    a learned router sends each token to its top-k experts ([JAX] "A dropless MoE minden
+           tokent feldolgoz" [dropless MoE processes every token]).  The pages give no formula:
+           slot j holds the j-th largest logit, ties go to the lower expert id, and the routing
+           weights are the softmax over the k kept logits.
+  plan     ragged per-expert groups ([JAX] "Az egyenetlen terhelés lassítja a tanítást" [uneven
+           load slows training]; per-expert token counts given as split sizes, [TE] "מומחים
+           מקובצים במקום לולאת Python" [grouped experts instead of a Python loop]): counts,
+           exclusive offsets, and a stable counting sort of the (token, slot) pairs by expert.
+  forward  dispatch, the first linear with a SwiGLU scaled by the routing weight, the second
+           linear, combine ([Mega] "Mega MoE คืออะไร?" [what is Mega MoE?]; [TE] "צמצום הזיכרון
+           ותקורות הכימות" [reducing memory and quantisation overheads]: GroupedLinear ->
+           ScaledSwiGLU -> GroupedLinear).  Every routed pair is computed at its real count:
+           no capacity, dropping or padding ([JAX] "A dropless MoE minden tokent feldolgoz";
+           "Csoportosított mátrixszorzás és összevont adatmozgatás" [grouped GEMM and fused
+           data movement]).
+  backward the gradient of that forward pass ([Prime] "Mit csinált a Prime Intellect?" [what
+           did Prime Intellect do?]: a backward for the fused MoE kernel): dx, dW1, dW2,
+           d(routing weights) and d(logits) through the top-k softmax.
+
+Conventions: W1[e] is [d, 2f] with gate columns [0, f) and up columns [f, 2f);
+SwiGLU(g, u) = silu(g) * u with silu(g) = g * sigmoid(g).  A pair p = t*k + j is slot j of
+token t.  Expert id -1 marks a slot that is not routed here (owned by another rank); such a
+pair is skipped everywhere.  All inputs must be finite.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# ------------------------------------------------------------------------------- routing
+def route(logits: np.ndarray, k: int):
+    """Top-k selection and softmax over the selected logits.
+
+    Returns (ids int32 [T, k], w fp64 [T, k]).  Slot 0 is the largest logit; among equal
+    logits the lower expert id comes first.  Selection is k rounds of "take the largest
+    remaining value" (np.argmax returns the first maximum, i.e. the lowest id on ties)."""
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    assert 1 <= k <= E
+    assert np.all(np.isfinite(L)), "logits must be finite"
+    taken = np.zeros((T, E), dtype=bool)
+    ids = np.empty((T, k), dtype=np.int32)
+    rows = np.arange(T)
+    for j in range(k):
+        cand = np.where(taken, -np.inf, L)
+        best = np.argmax(cand, axis=1)
+        ids[:, j] = best
+        taken[rows, best] = True
+    sel = L[rows[:, None], ids]                      # descending
+    z = np.exp(sel - sel[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)
+    return ids, w
+
+
+# ---------------------------------------------------------------------------------- plan
+@dataclass
+class Plan:
+    counts: np.ndarray    # int32 [E]        routed pairs per expert
+    offsets: np.ndarray   # int32 [E+1]      exclusive prefix sum of counts
+    perm: np.ndarray      # int32 [A]        sorted position -> pair index p
+    inv_perm: np.ndarray  # int32 [T*k]      pair index p -> sorted position, -1 if not routed
+
+
+def plan(ids: np.ndarray, E: int) -> Plan:
+    """Counting sort of pairs by expert.  Within an expert, pairs keep ascending pair index
+    (hence ascending token), which makes the order unique."""
+    flat = np.asarray(ids, dtype=np.int64).ravel()
+    assert np.all((flat >= -1) & (flat < E)), "expert ids must be in [-1, E)"
+    counts = np.zeros(E, dtype=np.int64)
+    for e in range(E):
+        counts[e] = np.count_nonzero(flat == e)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    perm = np.empty(offsets[E], dtype=np.int64)
+    for e in range(E):
+        perm[offsets[e]:offsets[e + 1]] = np.flatnonzero(flat == e)
+    inv_perm = np.full(flat.size, -1, dtype=np.int64)
+    inv_perm[perm] = np.arange(offsets[E])
+    return Plan(counts.astype(np.int32), offsets.astype(np.int32), perm.astype(np.int32),
+                inv_perm.astype(np.int32))
+
+
+def _expert_rows(pl: Plan, e: int, k: int):
+    P = pl.perm[pl.offsets[e]:pl.offsets[e + 1]].astype(np.int64)
+    return P, P // k            # pair indices, token rows
+
+
+# ------------------------------------------------------------------------------- forward
+def forward(x, W1, W2, ids, w, E=None, return_saved=False):
+    """y[t] = sum over routed slots j of w[t,j] * SwiGLU(x[t] W1[e]) W2[e], e = ids[t,j].
+
+    Inputs fp64 (already decoded): x [T,d], W1 [E,d,2f], W2 [E,f,d], ids [T,k], w [T,k]."""
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    E = W1.shape[0] if E is None else E
+    f = W2.shape[1]
+    k = ids.shape[1]
+    wf = np.asarray(w, np.float64).ravel()
+    pl = plan(ids, E)
+    y = np.zeros((T, d))
+    saved = {}
+    for e in range(E):
+        if pl.counts[e] == 0:
+            continue
+        P, R = _expert_rows(pl, e, k)
+        Xe = x[R]
+        He = Xe @ W1[e]
+        G, U = He[:, :f], He[:, f:]
+        a = G * _sigmoid(G) * U
+        Oe = a @ W2[e]
+        np.add.at(y, R, wf[P][:, None] * Oe)
+        if return_saved:
+            saved[e] = (G, U, a, Oe)
+    return (y, pl, saved) if return_saved else y
+
+
+# ------------------------------------------------------------------------------ backward
+def backward(x, W1, W2, ids, w, dy, logits_routed=True):
+    """Gradients of L = sum(dy * y) for the forward above.
+
+    Returns dict with dx [T,d], dW1 [E,d,2f], dW2 [E,f,d], d_topk_w [T,k] (0 on unrouted
+    slots) and, when the weights came from route() (logits_routed=True), d_logits [T,E]
+    through the softmax over the k selected logits (0 off the selected set)."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    T, d = x.shape
+    E = W1.shape[0]
+    f = W2.shape[1]
+    k = ids.shape[1]
+    wf = np.asarray(w, np.float64).ravel()
+    pl = plan(ids, E)
+    dx = np.zeros((T, d))
+    dW1 = np.zeros(W1.shape)
+    dW2 = np.zeros(W2.shape)
+    dw = np.zeros(T * k)
+    for e in range(E):
+        if pl.counts[e] == 0:
+            continue                                   # an empty expert has zero gradient
+        P, R = _expert_rows(pl, e, k)
+        Xe = x[R]
+        He = Xe @ W1[e]
+        G, U = He[:, :f], He[:, f:]
+        sg = _sigmoid(G)
+        S = G * sg                                     # silu(g)
+        a = S * U
+        Oe = a @ W2[e]
+        dYe = dy[R]
+        dw[P] = np.sum(dYe * Oe, axis=1)               # y is linear in each routing weight
+        dOe = wf[P][:, None] * dYe
+        dW2[e] = a.T @ dOe
+        da = dOe @ W2[e].T
+        dG = da * U * sg * (1.0 + G * (1.0 - sg))      # d silu / dg = sig * (1 + g (1 - sig))
+        dU = da * S
+        dH = np.concatenate([dG, dU], axis=1)
+        dW1[e] = Xe.T @ dH
+        np.add.at(dx, R, dH @ W1[e].T)
+    out = dict(dx=dx, dW1=dW1, dW2=dW2, d_topk_w=dw.reshape(T, k), plan=pl)
+    if logits_routed:
+        wm = np.asarray(w, np.float64)
+        dwm = dw.reshape(T, k)
+        inner = np.sum(wm * dwm, axis=1, keepdims=True)
+        dl = np.zeros((T, E))
+        rows = np.arange(T)[:, None]
+        dl[rows, ids] = wm * (dwm - inner)             # softmax Jacobian over the kept logits
+        out["d_logits"] = dl
+    return out
+
+
+# --------------------------------------------------------- per-entry forms (large inputs)
+# At full size the tests compare sampled outputs.  These functions compute single rows or
+# single gradient entries from the same definitions, touching only the rows they need.
+def token_forward(x_row, W1, W2, ids_row, w_row):
+    """y[t] for one token: sum_j w_j * SwiGLU(x_t W1[e_j]) W2[e_j] over routed slots."""
+    f = W2.shape[1]
+    y = np.zeros(x_row.shape[0])
+    for e, wj in zip(ids_row, w_row):
+        if e < 0:
+            continue
+        h = x_row @ W1[e]
+        g, u = h[:f], h[f:]
+        y += wj * ((g * _sigmoid(g) * u) @ W2[e])
+    return y
+
+
+def token_backward(x_row, W1, W2, ids_row, w_row, dy_row):
+    """(dx[t], d_topk_w[t, :]) for one token."""
+    f = W2.shape[1]
+    dx = np.zeros(x_row.shape[0])
+    dw = np.zeros(len(ids_row))
+    for j, (e, wj) in enumerate(zip(ids_row, w_row)):
+        if e < 0:
+            continue
+        h = x_row @ W1[e]
+        g, u = h[:f], h[f:]
+        sg = _sigmoid(g)
+        s = g * sg
+        a = s * u
+        dw[j] = dy_row @ (a @ W2[e])
+        da = wj * (W2[e] @ dy_row)
+        dg = da * u * sg * (1.0 + g * (1.0 - sg))
+        du = da * s
+        dx += W1[e] @ np.concatenate([dg, du])
+    return dx, dw
+
+
+def weight_grad_entries(x, W1, W2, ids, w, dy, e, rows_i, cols_j, which):
+    """Selected entries of dW1[e] (which='dW1', i over d, j over 2f) or dW2[e] (which='dW2',
+    i over f, j over d), computed from the expert's token rows only."""
+    k = ids.shape[1]
+    f = W2.shape[1]
+    flat = np.asarray(ids).ravel()
+    P = np.flatnonzero(flat == e)
+    if P.size == 0:
+        return np.zeros(len(rows_i))
+    R = P // k
+    wv = np.asarray(w, np.float64).ravel()[P]
+    Xe = np.asarray(x, np.float64)[R]
+    dYe = np.asarray(dy, np.float64)[R]
+    out = np.empty(len(rows_i))
+    for n, (i, j) in enumerate(zip(rows_i, cols_j)):
+        if which == "dW2":
+            g = Xe @ W1[e][:, i]
+            u = Xe @ W1[e][:, f + i]
+            a_i = g * _sigmoid(g) * u
+            out[n] = np.sum(a_i * wv * dYe[:, j])
+        else:
+            c = j % f                                   # column pair (gate c, up f + c)
+            g = Xe @ W1[e][:, c]
+            u = Xe @ W1[e][:, f + c]
+            sg = _sigmoid(g)
+            da = wv * (dYe @ W2[e][c, :])
+            dh = da * u * sg * (1.0 + g * (1.0 - sg)) if j < f else da * g * sg
+            out[n] = np.sum(Xe[:, i] * dh)
+    return out
+
+
+def d_logits_from_dw(w, dw, ids, E):
+    """d_logits[t, ids[t,j]] = w[t,j] * (dw[t,j] - sum_i w[t,i] dw[t,i]); zero elsewhere."""
+    w = np.asarray(w, np.float64)
+    dw = np.asarray(dw, np.float64)
+    T = w.shape[0]
+    inner = np.sum(w * dw, axis=1, keepdims=True)
+    dl = np.zeros((T, E))
+    dl[np.arange(T)[:, None], ids] = w * (dw - inner)
+    return dl
