@@ -1,0 +1,300 @@
+// C ABI (include/moe.h): host-side validation, workspace carving and stream-ordered launches.
+// Nothing here synchronises the host or reads device memory.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al256p(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+int check_dims(const moe_dims* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->reserved != 0) return MOE_ERR_SHAPE;
+  if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k < 1 || d->k > d->E || d->k > 64) return MOE_ERR_SHAPE;
+  if (d->d <= 0 || d->f <= 0 || d->d % 128 || d->f % 128 || d->d > 65536 || d->f > 65536) return MOE_ERR_SHAPE;
+  if (d->T * d->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3) return MOE_ERR_DTYPE;
+  // launch grids of the ragged GEMMs must fit in 32 bits
+  const int64_t A = d->T * d->k;
+  const int64_t rows = (A + kGemmBM - 1) / kGemmBM + (A < d->E ? A : d->E);
+  if (rows * (d->f / 64 > d->d / 128 ? d->f / 64 : d->d / 128) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+MoeShape shape_of(const moe_dims* d) {
+  return MoeShape{(int)d->T, (int)d->d, (int)d->f, (int)d->E, (int)d->k};
+}
+
+struct FwdLayout {
+  size_t tiles, ntiles, op, total;
+};
+struct BwdLayout {
+  size_t tiles, ntiles, dH, dXp, dwp, total;
+};
+struct SavedLayout {
+  size_t H, As, total;
+};
+
+FwdLayout fwd_layout(const moe_dims* d) {
+  const int64_t A = d->T * d->k;
+  FwdLayout L{};
+  size_t off = 0;
+  L.tiles = off;
+  off += al256((size_t)max_row_tiles(A, (int)d->E, kGemmBM) * sizeof(int2) + 16);
+  L.ntiles = off;
+  off += 256;
+  L.op = off;
+  off += al256((size_t)A * d->d * 2);
+  L.total = off;
+  return L;
+}
+
+BwdLayout bwd_layout(const moe_dims* d) {
+  const int64_t A = d->T * d->k;
+  BwdLayout L{};
+  size_t off = 0;
+  L.tiles = off;
+  off += al256((size_t)max_row_tiles(A, (int)d->E, kGemmBM) * sizeof(int2) + 16);
+  L.ntiles = off;
+  off += 256;
+  L.dH = off;
+  off += al256((size_t)A * 2 * d->f * 2);
+  L.dXp = off;
+  off += al256((size_t)A * d->d * 2);
+  L.dwp = off;
+  off += al256((size_t)A * (d->f / kDactBN) * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+SavedLayout saved_layout(const moe_dims* d) {
+  const int64_t A = d->T * d->k;
+  SavedLayout L{};
+  L.H = 0;
+  L.As = al256((size_t)A * 2 * d->f * 2);
+  L.total = L.As + al256((size_t)A * d->f * 2);
+  return L;
+}
+
+int hip_status(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_stage_hook g_hook = nullptr;
+void* g_hook_user = nullptr;
+
+// Enqueue one stage, bracketed by the profiling hook when one is set.
+#define MOE_TRY(name, expr)                                   \
+  do {                                                        \
+    if (g_hook) g_hook(name, 1, (void*)st, g_hook_user);      \
+    int _rc = hip_status(expr);                               \
+    if (g_hook) g_hook(name, 0, (void*)st, g_hook_user);      \
+    if (_rc != MOE_OK) return _rc;                            \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_bytes(const moe_dims* dims, int which, size_t* out) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!out) return MOE_ERR_NULL;
+  switch (which) {
+    case MOE_WS_ROUTE: *out = al256(plan_ws_bytes(dims->T * dims->k, dims->E)); return MOE_OK;
+    case MOE_WS_FORWARD: *out = fwd_layout(dims).total; return MOE_OK;
+    case MOE_WS_BACKWARD: *out = bwd_layout(dims).total; return MOE_OK;
+    default: return MOE_ERR_SHAPE;
+  }
+}
+
+int moe_saved_bytes(const moe_dims* dims, size_t* out) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!out) return MOE_ERR_NULL;
+  *out = saved_layout(dims).total;
+  return MOE_OK;
+}
+
+int moe_plan(const moe_dims* dims, const int32_t* topk_ids, int32_t* counts, int32_t* offsets, int32_t* perm,
+             int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  const int64_t A = dims->T * dims->k;
+  const size_t need = al256(plan_ws_bytes(A, dims->E));
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (A > 0 && (!topk_ids || !perm || !inv_perm)) return MOE_ERR_NULL;
+  if (need > 0 && !ws) return MOE_ERR_NULL;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (ws && !al256p(ws)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("plan", launch_plan(topk_ids, A, (int)dims->E, counts, offsets, perm, inv_perm, ws, st));
+
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims* dims, const float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+              int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  const int64_t A = dims->T * dims->k;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (A > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv_perm)) return MOE_ERR_NULL;
+  const size_t need = al256(plan_ws_bytes(A, dims->E));
+  if (need > 0 && !ws) return MOE_ERR_NULL;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (ws && !al256p(ws)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("router", launch_router(logits, (int)dims->T, (int)dims->E, (int)dims->k, topk_ids, topk_w, st));
+  MOE_TRY("plan", launch_plan(topk_ids, A, (int)dims->E, counts, offsets, perm, inv_perm, ws, st));
+
+  return MOE_OK;
+}
+
+int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const void* W1, const float* W1_scale,
+                const void* W2, const float* W2_scale, const float* topk_w, const int32_t* offsets,
+                const int32_t* perm, const int32_t* inv_perm, void* y, void* saved, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (x_scale || W1_scale || W2_scale) return MOE_ERR_DTYPE;
+  if (dims->T == 0) return MOE_OK;  // an empty layer has nothing to compute
+  if (!x || !W1 || !W2 || !topk_w || !offsets || !perm || !inv_perm || !y || !saved || !ws) return MOE_ERR_NULL;
+  const FwdLayout L = fwd_layout(dims);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!al16(x) || !al16(W1) || !al16(W2) || !al16(y) || !al256p(saved) || !al256p(ws)) return MOE_ERR_ALIGN;
+  const MoeShape s = shape_of(dims);
+  const SavedLayout SL = saved_layout(dims);
+  char* w = (char*)ws;
+  char* sv = (char*)saved;
+  int2* tiles = (int2*)(w + L.tiles);
+  int32_t* ntiles = (int32_t*)(w + L.ntiles);
+  uint16_t* Op = (uint16_t*)(w + L.op);
+  uint16_t* H = (uint16_t*)(sv + SL.H);
+  uint16_t* As = (uint16_t*)(sv + SL.As);
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kGemmBM, tiles, ntiles, st));
+  MOE_TRY("gemm_up", launch_gemm_up(s, (const uint16_t*)x, (const uint16_t*)W1, topk_w, offsets, perm, tiles, ntiles, H, As, st));
+  MOE_TRY("gemm_down", launch_gemm_down(s, As, (const uint16_t*)W2, offsets, perm, tiles, ntiles, Op, st));
+  MOE_TRY("combine", launch_combine(Op, inv_perm, s.T, s.d, s.k, (uint16_t*)y, st));
+
+  return MOE_OK;
+}
+
+int moe_backward(const moe_dims* dims, const void* dy, const void* x, const float* x_scale, const void* W1,
+                 const float* W1_scale, const void* W2, const float* W2_scale, const int32_t* topk_ids,
+                 const float* topk_w, const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm,
+                 const void* saved, void* dx, void* dW1, void* dW2, float* d_topk_w, float* d_logits, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (x_scale || W1_scale || W2_scale) return MOE_ERR_DTYPE;
+  if (dims->T == 0) {
+    // no routed pair: every expert's weight gradient is exactly zero, nothing else to write
+    if (!offsets || !dW1 || !dW2) return MOE_ERR_NULL;
+    if (!al16(dW1) || !al16(dW2)) return MOE_ERR_ALIGN;
+    const MoeShape s = shape_of(dims);
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, nullptr, nullptr, offsets, nullptr, (uint16_t*)dW2, st));
+    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, nullptr, nullptr, offsets, nullptr, (uint16_t*)dW1, st));
+
+    return MOE_OK;
+  }
+  if (!dy || !x || !W1 || !W2 || !topk_w || !offsets || !perm || !inv_perm || !saved || !dx || !dW1 || !dW2 ||
+      !d_topk_w || !ws)
+    return MOE_ERR_NULL;
+  if (d_logits && !topk_ids) return MOE_ERR_NULL;
+  const BwdLayout L = bwd_layout(dims);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!al16(dy) || !al16(x) || !al16(W1) || !al16(W2) || !al16(dx) || !al16(dW1) || !al16(dW2) || !al256p(saved) ||
+      !al256p(ws))
+    return MOE_ERR_ALIGN;
+  const MoeShape s = shape_of(dims);
+  const SavedLayout SL = saved_layout(dims);
+  char* w = (char*)ws;
+  const char* sv = (const char*)saved;
+  int2* tiles = (int2*)(w + L.tiles);
+  int32_t* ntiles = (int32_t*)(w + L.ntiles);
+  uint16_t* dH = (uint16_t*)(w + L.dH);
+  uint16_t* dXp = (uint16_t*)(w + L.dXp);
+  float* dwp = (float*)(w + L.dwp);
+  const uint16_t* H = (const uint16_t*)(sv + SL.H);
+  const uint16_t* As = (const uint16_t*)(sv + SL.As);
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kGemmBM, tiles, ntiles, st));
+  MOE_TRY("gemm_dact", launch_gemm_dact(s, (const uint16_t*)dy, (const uint16_t*)W2, H, topk_w, offsets, perm, tiles, ntiles, dH,
+                           dwp, st));
+  MOE_TRY("gemm_dx", launch_gemm_dx(s, dH, (const uint16_t*)W1, offsets, perm, tiles, ntiles, dXp, st));
+  MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
+  MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, (uint16_t*)dW2, st));
+  MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, (uint16_t*)dW1, st));
+  MOE_TRY("dlogits", launch_dlogits(dwp, s.f / kDactBN, inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
+                                   st));
+
+  return MOE_OK;
+}
+
+int moe_permute(const moe_dims* dims, const void* x, const int32_t* perm, const int32_t* offsets, void* xp,
+                void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!x || !perm || !offsets || !xp) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(xp)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("permute", launch_permute((const uint16_t*)x, perm, offsets + dims->E, dims->T * dims->k, (int)dims->d,
+                                   (int)dims->k, (uint16_t*)xp, st));
+
+  return MOE_OK;
+}
+
+int moe_combine(const moe_dims* dims, const void* op, const int32_t* inv_perm, void* y, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!op || !inv_perm || !y) return MOE_ERR_NULL;
+  if (!al16(op) || !al16(y)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("combine", launch_combine((const uint16_t*)op, inv_perm, (int)dims->T, (int)dims->d, (int)dims->k,
+                                   (uint16_t*)y, st));
+
+  return MOE_OK;
+}
+
+int moe_set_stage_hook(moe_stage_hook hook, void* user) {
+  g_hook = hook;
+  g_hook_user = user;
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "dims outside the supported range";
+    case MOE_ERR_DTYPE: return "dtype not supported by this call";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_ALIGN: return "buffer not aligned (tensors 16 bytes, ws/saved 256 bytes)";
+    case MOE_ERR_HIP: return hipGetErrorString(g_last_hip);
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

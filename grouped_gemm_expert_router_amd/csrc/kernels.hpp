@@ -1,0 +1,59 @@
+// Host-side launchers of the MoE kernels (stream-ordered, no host synchronisation).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// routing and plan
+hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
+void plan_geometry(int64_t A, int* seg, int* S);
+size_t plan_ws_bytes(int64_t A, int64_t E);
+hipError_t launch_plan(const int32_t* ids, int64_t A, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv_perm, void* ws, hipStream_t st);
+hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int2* tiles, int32_t* ntiles, hipStream_t st);
+
+// grouped GEMMs (bf16 operands, fp32 accumulation)
+struct MoeShape {
+  int T, d, f, E, k;
+};
+
+// Row-tile height of the ragged-M grouped GEMMs (the tile table is built for it).
+constexpr int kGemmBM = 128;
+// Column-tile width of the activation-gradient GEMM (sets the number of d_topk_w partials).
+constexpr int kDactBN = 128;
+
+int max_row_tiles(int64_t A, int E, int BM);
+
+// GEMM1: H = x[perm/k] . W1[e] (gate|up), As = w * silu(gate) * up.
+hipError_t launch_gemm_up(const MoeShape& s, const uint16_t* x, const uint16_t* W1, const float* topk_w,
+                          const int32_t* offsets, const int32_t* perm, const int2* tiles, const int32_t* ntiles,
+                          uint16_t* H, uint16_t* As, hipStream_t st);
+// GEMM2: Op[perm[pos]] = As[pos] . W2[e]  (per-pair output in slot order).
+hipError_t launch_gemm_down(const MoeShape& s, const uint16_t* As, const uint16_t* W2, const int32_t* offsets,
+                            const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* Op,
+                            hipStream_t st);
+// dA: G = dy[perm/k] . W2[e]^T; epilogue -> dH (dSwiGLU) and d_topk_w partials.
+hipError_t launch_gemm_dact(const MoeShape& s, const uint16_t* dy, const uint16_t* W2, const uint16_t* H,
+                            const float* topk_w, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                            const int32_t* ntiles, uint16_t* dH, float* dwp, hipStream_t st);
+// dX: dXp[perm[pos]] = dH[pos] . W1[e]^T.
+hipError_t launch_gemm_dx(const MoeShape& s, const uint16_t* dH, const uint16_t* W1, const int32_t* offsets,
+                          const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* dXp,
+                          hipStream_t st);
+// Weight gradients (ragged K = the expert's rows):
+//   dW2[e] = As_e^T . dy[perm/k]_e     dW1[e] = x[perm/k]_e^T . dH_e
+hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t* dy, const int32_t* offsets,
+                           const int32_t* perm, uint16_t* dW2, hipStream_t st);
+hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t* dH, const int32_t* offsets,
+                           const int32_t* perm, uint16_t* dW1, hipStream_t st);
+
+// data movement and router backward
+hipError_t launch_permute(const uint16_t* x, const int32_t* perm, const int32_t* offsets, int64_t A, int d, int k,
+                          uint16_t* xp, hipStream_t st);
+hipError_t launch_combine(const uint16_t* op, const int32_t* inv_perm, int T, int d, int k, uint16_t* y,
+                          hipStream_t st);
+hipError_t launch_dlogits(const float* dwp, int nparts, const int32_t* inv_perm, const int32_t* ids,
+                          const float* topk_w, int T, int E, int k, float* d_topk_w, float* d_logits, hipStream_t st);
+
+}  // namespace moe

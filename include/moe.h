@@ -1,0 +1,161 @@
+/*
+ * moe.h — C ABI of a dropless mixture-of-experts layer (forward and backward) for AMD
+ * Instinct MI355X (gfx950).  Library: libmoe.so.
+ *
+ * Pages the operations are defined on (titles as published; headings translated in []):
+ *   [Prime] "Prime Mega MoE: tanításra is jó a DeepSeek MoE kernele" (neuraldaily.news)
+ *   [JAX]   "Az NVIDIA szerint tízszer gyorsabb lett a dropless MoE tanítása JAX-ban" (aihirek.info)
+ *   [TE]    "NVIDIA מציגה דרך יעילה לאמן מודלי MoE בביולוגיה" (sitech.ge)
+ *   [Mega]  the DeepGEMM "Mega MoE" announcement on itsolotime.com
+ *
+ * Notation: T tokens, d model dim, f expert FFN dim, E experts, k slots per token.  A pair
+ * p = t*k + j is slot j of token t.  A = T*k is the maximum number of routed pairs; buffers are
+ * sized by it, never by E x capacity (dropless: [JAX] "A dropless MoE minden tokent
+ * feldolgoz" [dropless MoE processes every token]).
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   x, dx, y, dy   bf16 [T, d]              (fp8: x is e4m3 [T, d] with x_scale fp32 [T, d/128])
+ *   W1, dW1        bf16 [E, d, 2f]          columns [0,f) are the gate, [f,2f) the up projection
+ *                                           (fp8: e4m3 with W1_scale fp32 [E, d/128, 2f/128])
+ *   W2, dW2        bf16 [E, f, d]           (fp8: e4m3 with W2_scale fp32 [E, f/128, d/128])
+ *   logits, d_logits  fp32 [T, E]
+ *   topk_ids       int32 [T, k]  slot j = j-th largest logit, ties to the lower id; -1 = the
+ *                                slot is not routed here (pre-routed input only)
+ *   topk_w, d_topk_w  fp32 [T, k]
+ *   counts         int32 [E]     routed pairs per expert
+ *   offsets        int32 [E+1]   exclusive prefix sum of counts; offsets[E] = routed pairs
+ *   perm           int32 [T*k]   sorted position -> pair p (entries >= offsets[E] unused)
+ *   inv_perm       int32 [T*k]   pair p -> sorted position, -1 for a slot that is not routed
+ * The sorted order is expert-major, then ascending pair index within an expert (a stable
+ * counting sort), which makes it unique and bit-reproducible.
+ *
+ * Conventions for every call:
+ *   - Ownership: the caller allocates every buffer (including `ws` workspace and the `saved`
+ *     forward->backward context).  The library allocates nothing and keeps no state between
+ *     calls; calls are re-entrant.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work
+ *     on it and return; nothing synchronises the host and no count leaves the device.
+ *   - Validation: arguments are checked on the host only.  Device contents are preconditions:
+ *     inputs finite, expert ids in [-1, E), a token's valid ids distinct.  Ids outside
+ *     [0, E) are treated as "not routed here".
+ *   - Errors: a negative MOE_ERR_* code is returned and nothing is enqueued; MOE_ERR_HIP means
+ *     a launch failed (moe_status_string() then names the HIP error).
+ *   - Shapes (MOE_ERR_SHAPE otherwise): T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64),
+ *     d and f positive multiples of 128 and at most 65536, T*k < 2^31.
+ *   - Alignment (MOE_ERR_ALIGN otherwise): tensors 16-byte aligned, ws and saved 256-byte
+ *     aligned (every torch/hipMalloc allocation is).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1 } moe_dtype;
+
+typedef struct {
+  int64_t T, d, f, E, k;
+  int32_t dtype; /* moe_dtype */
+  int32_t reserved; /* must be 0 */
+} moe_dims;
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,     /* dims outside the supported range */
+  MOE_ERR_DTYPE = -3,     /* dtype not supported by this call */
+  MOE_ERR_WORKSPACE = -4, /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = -5,       /* a HIP launch failed */
+  MOE_ERR_ALIGN = -6      /* a device buffer is not 16-byte aligned (ws and saved: 256) */
+};
+
+enum { MOE_WS_ROUTE = 0, MOE_WS_FORWARD = 1, MOE_WS_BACKWARD = 2 };
+
+/* Workspace bytes needed by moe_route/moe_plan (which = MOE_WS_ROUTE), moe_forward
+ * (MOE_WS_FORWARD) or moe_backward (MOE_WS_BACKWARD).  Host only. */
+int moe_workspace_bytes(const moe_dims* dims, int which, size_t* out);
+
+/* Bytes of the `saved` context moe_forward writes and moe_backward reads (the GEMM1 output
+ * H = [gate | up] and the scaled SwiGLU activations).  Host only. */
+int moe_saved_bytes(const moe_dims* dims, size_t* out);
+
+/* Top-k routing plus the expert plan.  Per token: the k largest logits (descending, ties to
+ * the lower expert id) and topk_w = softmax over those k logits in fp32 ([JAX] "A dropless MoE
+ * minden tokent feldolgoz": a learned router activates only the top-K experts per token).
+ * Then counts, offsets, perm and inv_perm as for moe_plan. */
+int moe_route(const moe_dims* dims, const float* logits, int32_t* topk_ids, float* topk_w,
+              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Expert plan for already-routed pairs: per-expert counts, their exclusive prefix sum and the
+ * stable counting sort of pairs by expert (ragged per-expert groups: [JAX] "Az egyenetlen
+ * terhelés lassítja a tanítást" [uneven load slows training]; per-expert counts as split
+ * sizes: [TE] "מומחים מקובצים במקום לולאת Python" [grouped experts instead of a Python loop]).
+ * Integer only, bit-exact and deterministic.  Ids -1 are skipped (inv_perm = -1). */
+int moe_plan(const moe_dims* dims, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+             int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward: y[t] = sum_j w[t,j] * (silu(x_t W1[e] gate) * (x_t W1[e] up)) W2[e], e = ids[t,j],
+ * over routed slots ([Mega] "Mega MoE คืออะไร?" [what is Mega MoE?]: dispatch, two linear layers,
+ * SwiGLU, combine; [TE] "צמצום הזיכרון ותקורות הכימות": GroupedLinear -> ScaledSwiGLU ->
+ * GroupedLinear).  The token gather is fused into the first grouped GEMM's operand loads, the
+ * routing weight into its SwiGLU epilogue, and the combine sums a token's k per-pair outputs in
+ * fp32 in slot order with one bf16 rounding.  Each expert is computed at its real row count
+ * ([JAX] "Csoportosított mátrixszorzás és összevont adatmozgatás" [grouped GEMM and fused data
+ * movement]).  `saved` (moe_saved_bytes) receives what moe_backward needs.  For
+ * dtype = MOE_FP8_E4M3 the *_scale arguments are required; for bf16 they must be NULL. */
+int moe_forward(const moe_dims* dims, const void* x, const float* x_scale,
+                const void* W1, const float* W1_scale, const void* W2, const float* W2_scale,
+                const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                const int32_t* inv_perm, void* y, void* saved, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Backward of moe_forward for L = sum(dy * y) ([Prime] "Mit csinált a Prime Intellect?" [what
+ * did Prime Intellect do?]: a backward pass for the fused MoE kernel).  Writes dx (bf16),
+ * dW1 and dW2 (bf16; an expert with no routed pair gets exactly zero), d_topk_w (fp32, 0 on
+ * unrouted slots) and, if d_logits is not NULL, d_logits[t, ids[t,j]] =
+ * w[t,j] * (d_topk_w[t,j] - sum_i w[t,i] d_topk_w[t,i]) and 0 elsewhere (the softmax over the
+ * kept logits; topk_ids is then required).  `saved` must come from moe_forward on the same
+ * inputs.  Every reduction has a fixed order, so results are bitwise reproducible. */
+int moe_backward(const moe_dims* dims, const void* dy, const void* x, const float* x_scale,
+                 const void* W1, const float* W1_scale, const void* W2, const float* W2_scale,
+                 const int32_t* topk_ids, const float* topk_w, const int32_t* offsets,
+                 const int32_t* perm, const int32_t* inv_perm, const void* saved, void* dx,
+                 void* dW1, void* dW2, float* d_topk_w, float* d_logits, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/* Dispatch on its own (bf16): xp[pos] = x[perm[pos] / k] for pos < offsets[E]; rows of xp at
+ * or past offsets[E] are left untouched.  xp is bf16 [T*k, d].  ([JAX] "Csoportosított
+ * mátrixszorzás és összevont adatmozgatás": dispatch sends tokens to their experts.)  The
+ * forward pass does not call it (its GEMM gathers rows directly); it exists for callers that
+ * want expert-sorted activations. */
+int moe_permute(const moe_dims* dims, const void* x, const int32_t* perm, const int32_t* offsets,
+                void* xp, void* stream);
+
+/* Combine on its own (bf16): y[t] = sum over j = 0..k-1 with inv_perm[t*k+j] >= 0 of
+ * op[t*k+j], summed in fp32 in ascending j and rounded once to bf16 (combine gathers the
+ * results back and restores token order: [JAX] "Az egyenetlen terhelés lassítja a
+ * tanítást").  op is bf16 [T*k, d] in pair (slot) order. */
+int moe_combine(const moe_dims* dims, const void* op, const int32_t* inv_perm, void* y,
+                void* stream);
+
+/* Optional profiling hook (process-wide; none by default).  When set, each call invokes
+ * hook(stage, 1, stream, user) on the calling thread right before it enqueues a stage's kernel
+ * and hook(stage, 0, stream, user) right after, so a profiler can record stream events around
+ * every kernel.  `stage` is a static string naming the kernel ("gemm_up", "combine", ...).
+ * Pass NULL to remove the hook.  Setting it while another thread is inside a call races. */
+typedef void (*moe_stage_hook)(const char* stage, int begin, void* stream, void* user);
+int moe_set_stage_hook(moe_stage_hook hook, void* user);
+
+/* Static string for a status code (for MOE_ERR_HIP: the last HIP error on this thread). */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point, and
+every host-side validation path returns its error code without launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_gemm_expert_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return moe.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == sorted(moe.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (moe.MOE_OK, moe.MOE_ERR_NULL, moe.MOE_ERR_SHAPE, moe.MOE_ERR_DTYPE, moe.MOE_ERR_WORKSPACE,
+               moe.MOE_ERR_ALIGN):
+        assert len(moe.status_string(st)) >= 2
+    assert moe.status_string(-99) == "unknown status"
+
+
+def sz(lib, dm, which):
+    out = ctypes.c_size_t(0)
+    rc = lib.moe_workspace_bytes(ctypes.byref(dm), which, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("bad", [
+    dict(k=0), dict(k=9), dict(E=0), dict(E=1025, k=2), dict(k=65, E=128), dict(d=100), dict(f=64),
+    dict(T=-1), dict(d=0), dict(T=(1 << 31) // 2, k=2),
+])
+def test_shape_errors(lib, bad):
+    p = dict(T=64, d=128, f=256, E=8, k=2)
+    p.update(bad)
+    dm = moe.dims(**p)
+    assert sz(lib, dm, moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
+
+
+def test_dtype_and_reserved_errors(lib):
+    dm = moe.dims(64, 128, 256, 8, 2, dtype=7)
+    assert sz(lib, dm, moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_DTYPE
+    dm = moe.dims(64, 128, 256, 8, 2)
+    dm.reserved = 1
+    assert sz(lib, dm, moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
+    assert lib.moe_workspace_bytes(None, 0, None) == moe.MOE_ERR_NULL
+    assert lib.moe_workspace_bytes(ctypes.byref(moe.dims(64, 128, 256, 8, 2)), 0, None) == moe.MOE_ERR_NULL
+    assert sz(lib, moe.dims(64, 128, 256, 8, 2), 3)[0] == moe.MOE_ERR_SHAPE
+
+
+def test_workspace_sizes_scale_with_pairs_not_capacity(lib):
+    small = sz(lib, moe.dims(64, 128, 256, 8, 2), moe.MOE_WS_FORWARD)[1]
+    big = sz(lib, moe.dims(128, 128, 256, 8, 2), moe.MOE_WS_FORWARD)[1]
+    assert 0 < small < big
+    out = ctypes.c_size_t(0)
+    assert lib.moe_saved_bytes(ctypes.byref(moe.dims(64, 128, 256, 8, 2)), ctypes.byref(out)) == 0
+    # saved context = H [A, 2f] + As [A, f] in bf16, nothing sized by experts x capacity
+    assert out.value == 64 * 2 * 2 * 256 * 2 + 64 * 2 * 256 * 2
+    # zero tokens is a legal (empty) layer
+    assert sz(lib, moe.dims(0, 128, 256, 8, 2), moe.MOE_WS_FORWARD)[0] == 0
+
+
+FAKE = 1 << 20  # a non-null, 256-aligned address that is never dereferenced on error paths
+
+
+def test_route_and_plan_argument_errors(lib):
+    dm = moe.dims(64, 128, 256, 8, 2)
+    rc, need = sz(lib, dm, moe.MOE_WS_ROUTE)
+    assert rc == 0 and need > 0
+    args = [FAKE] * 7
+    assert lib.moe_route(ctypes.byref(dm), None, *args, need, None) == moe.MOE_ERR_NULL
+    assert lib.moe_route(ctypes.byref(dm), FAKE, *args[:-1], None, need, None) == moe.MOE_ERR_NULL
+    assert lib.moe_route(ctypes.byref(dm), FAKE, *args, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(dm), FAKE, *args[:-1], FAKE + 8, need, None) == moe.MOE_ERR_ALIGN
+    assert lib.moe_plan(ctypes.byref(dm), None, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == moe.MOE_ERR_NULL
+    assert lib.moe_plan(ctypes.byref(dm), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == moe.MOE_ERR_WORKSPACE
+    bad = moe.dims(64, 128, 256, 8, 9)
+    assert lib.moe_route(ctypes.byref(bad), FAKE, *args, need, None) == moe.MOE_ERR_SHAPE
+
+
+def test_forward_backward_argument_errors(lib):
+    dm = moe.dims(64, 128, 256, 8, 2)
+    _, wf = sz(lib, dm, moe.MOE_WS_FORWARD)
+    _, wb = sz(lib, dm, moe.MOE_WS_BACKWARD)
+    F = FAKE
+    fwd = lambda **o: lib.moe_forward(ctypes.byref(o.get("dm", dm)), o.get("x", F), o.get("xs", None), F, None, F,
+                                      None, F, F, F, F, o.get("y", F), F, F, o.get("ws", wf), None)
+    assert fwd(x=None) == moe.MOE_ERR_NULL
+    assert fwd(y=None) == moe.MOE_ERR_NULL
+    assert fwd(xs=F) == moe.MOE_ERR_DTYPE                 # scales with bf16
+    assert fwd(ws=wf - 1) == moe.MOE_ERR_WORKSPACE
+    assert fwd(x=F + 2) == moe.MOE_ERR_ALIGN
+    fp8 = moe.dims(64, 128, 256, 8, 2, dtype=moe.MOE_FP8_E4M3)
+    _, wf8 = sz(lib, fp8, moe.MOE_WS_FORWARD)
+    assert lib.moe_forward(ctypes.byref(fp8), F, None, F, F, F, F, F, F, F, F, F, F, F, wf8, None) in (
+        moe.MOE_ERR_DTYPE, moe.MOE_ERR_NULL)               # fp8 needs every scale
+    bwd = lambda **o: lib.moe_backward(ctypes.byref(dm), F, F, None, F, None, F, None, o.get("ids", F), F, F, F, F, F,
+                                       F, F, F, o.get("dtw", F), o.get("dl", F), F, o.get("ws", wb), None)
+    assert bwd(dtw=None) == moe.MOE_ERR_NULL
+    assert bwd(ids=None) == moe.MOE_ERR_NULL               # d_logits requested without ids
+    assert bwd(ws=wb - 1) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(ctypes.byref(dm), None, F, F, None) == moe.MOE_ERR_NULL
+    assert lib.moe_permute(ctypes.byref(dm), F, F, F, None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_combine(ctypes.byref(dm), F + 4, F, F, None) == moe.MOE_ERR_ALIGN
