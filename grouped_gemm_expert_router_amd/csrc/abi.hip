@@ -73,7 +73,7 @@ BwdLayout bwd_layout(const moe_dims* d) {
   L.dXp = off;
   off += al256((size_t)A * d->d * 2);
   L.dwp = off;
-  off += al256((size_t)A * (d->f / kDactBN) * sizeof(float));
+  off += al256((size_t)A * (d->f / dact_bn((int)d->f)) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -245,7 +245,7 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
   MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, (uint16_t*)dW2, st));
   MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, (uint16_t*)dW1, st));
-  MOE_TRY("dlogits", launch_dlogits(dwp, s.f / kDactBN, inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
+  MOE_TRY("dlogits", launch_dlogits(dwp, s.f / dact_bn(s.f), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
                                    st));
 
   return MOE_OK;

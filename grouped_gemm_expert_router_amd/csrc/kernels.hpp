@@ -19,9 +19,10 @@ struct MoeShape {
 };
 
 // Row-tile height of the ragged-M grouped GEMMs (the tile table is built for it).
-constexpr int kGemmBM = 128;
-// Column-tile width of the activation-gradient GEMM (sets the number of d_topk_w partials).
-constexpr int kDactBN = 128;
+constexpr int kGemmBM = 256;
+// Column-tile width of the activation-gradient GEMM for expert FFN dim f; f / dact_bn(f)
+// partial sums of d_topk_w are written per routed pair.
+int dact_bn(int f);
 
 int max_row_tiles(int64_t A, int E, int BM);
 
