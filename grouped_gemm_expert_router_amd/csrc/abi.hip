@@ -40,7 +40,7 @@ struct FwdLayout {
   size_t tiles, ntiles, op, total;
 };
 struct BwdLayout {
-  size_t tiles, ntiles, dH, dXp, dwp, total;
+  size_t tiles, ntiles, tokrow, dH, dXp, dwp, total;
 };
 struct SavedLayout {
   size_t H, As, total;
@@ -68,6 +68,8 @@ BwdLayout bwd_layout(const moe_dims* d) {
   off += al256((size_t)max_row_tiles(A, (int)d->E, kGemmBM) * sizeof(int2) + 16);
   L.ntiles = off;
   off += 256;
+  L.tokrow = off;
+  off += al256((size_t)(A + kTokrowPad) * sizeof(int32_t));
   L.dH = off;
   off += al256((size_t)A * 2 * d->f * 2);
   L.dXp = off;
@@ -212,8 +214,8 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
     if (!al16(dW1) || !al16(dW2)) return MOE_ERR_ALIGN;
     const MoeShape s = shape_of(dims);
     hipStream_t st = (hipStream_t)stream;
-    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, nullptr, nullptr, offsets, nullptr, (uint16_t*)dW2, st));
-    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, nullptr, nullptr, offsets, nullptr, (uint16_t*)dW1, st));
+    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, nullptr, nullptr, offsets, nullptr, nullptr, (uint16_t*)dW2, st));
+    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, nullptr, nullptr, offsets, nullptr, nullptr, (uint16_t*)dW1, st));
 
     return MOE_OK;
   }
@@ -235,6 +237,7 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   uint16_t* dH = (uint16_t*)(w + L.dH);
   uint16_t* dXp = (uint16_t*)(w + L.dXp);
   float* dwp = (float*)(w + L.dwp);
+  int32_t* tokrow = (int32_t*)(w + L.tokrow);
   const uint16_t* H = (const uint16_t*)(sv + SL.H);
   const uint16_t* As = (const uint16_t*)(sv + SL.As);
   hipStream_t st = (hipStream_t)stream;
@@ -243,8 +246,9 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                            dwp, st));
   MOE_TRY("gemm_dx", launch_gemm_dx(s, dH, (const uint16_t*)W1, offsets, perm, tiles, ntiles, dXp, st));
   MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
-  MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, (uint16_t*)dW2, st));
-  MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, (uint16_t*)dW1, st));
+  MOE_TRY("tokrow", launch_tokrow(perm, offsets, s.E, (int64_t)s.T * s.k, s.k, tokrow, st));
+  MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, (uint16_t*)dW2, st));
+  MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, tokrow, (uint16_t*)dW1, st));
   MOE_TRY("dlogits", launch_dlogits(dwp, s.f / dact_bn(s.f), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
                                    st));
 

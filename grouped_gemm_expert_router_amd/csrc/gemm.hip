@@ -38,6 +38,7 @@ struct GemmArgs {
   int kslots, f;
   const int32_t* offsets;
   const int32_t* perm;
+  const int32_t* tokrow;  // ragged K: token row of each sorted position (perm[pos] / k)
   const int2* tiles;
   const int32_t* ntiles;
   int gatherA, gatherB;  // operand rows come from token perm[pos] / k instead of position pos
@@ -55,34 +56,6 @@ struct GemmArgs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// v if ok else 0
-__device__ __forceinline__ u32x4 keep_if(u32x4 v, bool ok) {
-  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-  return v & m;
-}
-
-// Write a 4(k) x 8(n) block, loaded as 4 rows of 8 consecutive n, into the K-contiguous LDS
-// tile: LDS row n gets 4 consecutive k (8 bytes) at k offset 4*kb.
-template <int BK>
-__device__ __forceinline__ void store_transposed(uint16_t* lds, int n_base, int kb, u32x4 v0, u32x4 v1, u32x4 v2,
-                                                 u32x4 v3) {
-  constexpr int KCH = BK / 8;
-  const int chunk = kb >> 1, half = kb & 1;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t r0 = v0[w], r1 = v1[w], r2 = v2[w], r3 = v3[w];
-    u32x2 ce, co;
-    ce.x = (r0 & 0xFFFFu) | (r1 << 16);
-    ce.y = (r2 & 0xFFFFu) | (r3 << 16);
-    co.x = (r0 >> 16) | (r1 & 0xFFFF0000u);
-    co.y = (r2 >> 16) | (r3 & 0xFFFF0000u);
-    int n = n_base + 2 * w;
-    *(u32x2*)&lds[n * BK + ((chunk ^ (n % KCH)) * 8) + half * 4] = ce;
-    n += 1;
-    *(u32x2*)&lds[n * BK + ((chunk ^ (n % KCH)) * 8) + half * 4] = co;
-  }
-}
-
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
   return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
 }
@@ -97,31 +70,92 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return x * q + min(x, r) + i;
 }
 
-template <int MODE, int BM, int BN, int BK, int WM, int WN, int OCC>
-__global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g) {
-  constexpr int NTH = 256;
-  static_assert(WM * WN == 4, "four waves");
-  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int KCH = BK / 8;
-  constexpr bool RAGGED_K = (MODE == M_WG);
-  constexpr bool B_KC = (MODE == M_DACT || MODE == M_DX);
-  static_assert(MODE != M_UP || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
+// ---------------------------------------------------------------- LDS DMA and barriers
+// global_load_lds_dwordx4 copies each lane's 16 bytes to LDS at m0 + 16*lane.  It is issued
+// through inline asm so the compiler's wait-count pass does not make every LDS read wait for
+// all DMA in flight; the kernel waits explicitly (vm_wait_barrier) before the barrier that
+// publishes a stage.  One wait state separates the m0 write from the DMA.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_byte_addr)
+               : "memory", "m0");
+}
 
-  // One LDS arena: two operand stages during the K loop, then the fp32 staging band of the
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+// Operand tiles in LDS (16-byte chunks, XOR-swizzled so the 16 lanes an LDS cycle serves hit
+// 16 distinct 16-byte bank groups of the 64-bank LDS):
+//   KM: [row][BK=32] for K-contiguous sources; row = 64 bytes = 4 chunks; chunk c of row r
+//       lives at chunk c ^ ((r >> 2) & 3).  MFMA operand = one ds_read_b128.
+//   KN: [k][C] for sources contiguous along M or N; k row = 2C bytes; chunk c of k row r lives
+//       at chunk c ^ (4 * (r & 3)).  MFMA operand = two ds_read_b64_tr_b16: within a 16-lane
+//       group, lane s supplies the address of (k = k0 + s/4, col = c0 + 4*(s%4)) and lane i
+//       receives the 4 values (k0..k0+3, c0 + i).
+__device__ __forceinline__ uint32_t km_off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+template <int C>
+__device__ __forceinline__ uint32_t kn_off(int kr, int col) {
+  return kr * (2 * C) + ((((col >> 3) ^ (4 * (kr & 3)))) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ bf16x8_t read_km(uint32_t base, int row, int c) {
+  return *(const LDS_AS bf16x8_t*)(uintptr_t)(base + km_off(row, c));
+}
+// 32-column fragment at column cbase, k16 step kk: lane holds column cbase + lane%32 and
+// k = 16*kk + 8*(lane/32) + 0..7.
+template <int C>
+__device__ __forceinline__ bf16x8_t read_kn(uint32_t base, int cbase, int kk, int lane) {
+  const int grp = lane >> 4, i16 = lane & 15;
+  const int col = cbase + 16 * (grp & 1) + 4 * (i16 & 3);
+  const int kr0 = 16 * kk + 8 * (grp >> 1) + (i16 >> 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)(base + kn_off<C>(kr0, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)(base + kn_off<C>(kr0 + 4, col)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int MODE, int BM, int BN, int OCC>
+__global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g) {
+  constexpr int NTH = 256, BK = 32, S = 4, WM = 2, WN = 2;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr bool RAGGED_K = (MODE == M_WG);
+  constexpr bool A_KN = RAGGED_K;                              // A stored [k][m]
+  constexpr bool B_KN = !(MODE == M_DACT || MODE == M_DX);     // B stored [k][n]
+  static_assert(MODE != M_UP || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int QA = BM / 64, QB = BN / 64;  // DMA instructions per thread per tile
+  constexpr int DPT = QA + QB;
+  static_assert(DPT * (S - 2) <= 63, "vmcnt range");
+
+  // One LDS arena: S operand stages during the K loop, then the fp32 staging band of the
   // epilogue (64 rows x BN columns, rows padded by 4 floats against bank conflicts).
   constexpr int CPAD = BN + 4;
-  constexpr int STAGE_BYTES = 2 * (BM + BN) * BK * 2;
   constexpr int CBAND_BYTES = 2 * 32 * CPAD * 4;
-  static_assert(WM == 2, "the epilogue band holds one 32-row fragment block of each of 2 wave rows");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[STAGE_BYTES > CBAND_BYTES ? STAGE_BYTES : CBAND_BYTES];
-  uint16_t (*sA)[BM * BK] = reinterpret_cast<uint16_t (*)[BM * BK]>(smem);
-  uint16_t (*sB)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(smem + 2 * BM * BK * 2);
+  constexpr int ARENA = S * STAGE > CBAND_BYTES ? S * STAGE : CBAND_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ARENA];
   float* cband = reinterpret_cast<float*>(smem);
   __shared__ float s_w[RAGGED_K ? 1 : BM];
   __shared__ int s_slot[RAGGED_K ? 1 : BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
 
   // ------------------------------------------------------------------ tile coordinates
   int e, m0, mrows, n0, nt, kbeg, kend;
@@ -134,8 +168,9 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
     m0 = ((lid % per_e) / nN) * BM;
     mrows = BM;
     n0 = nt * BN;
-    kbeg = g.offsets[e];
-    kend = g.offsets[e + 1];
+    const CONST_AS int32_t* off4 = (const CONST_AS int32_t*)g.offsets;
+    kbeg = off4[e];
+    kend = off4[e + 1];
   } else {
     const int nN = (MODE == M_UP) ? g.f / (BN / 2) : g.N / BN;
     nt = lid % nN;
@@ -159,127 +194,98 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
       s_w[r] = wv;
     }
   }
-
-  // ------------------------------------------------------------------ operand loaders
-  // K-contiguous rows: thread owns 16-byte chunk c of rows tid/KCH + i*(NTH/KCH).
-  constexpr int A_PER = RAGGED_K ? 1 : BM * KCH / NTH;
-  constexpr int B_PER = B_KC ? BN * KCH / NTH : 1;
-  // K-strided 4x8 units: thread owns k rows 4*kb..4*kb+3 and 8 columns of unit u.
-  constexpr int UK = BK / 4;
-  constexpr int A_UNITS = RAGGED_K ? (UK * (BM / 8)) / NTH : 1;
-  constexpr int B_UNITS = B_KC ? 1 : (UK * (BN / 8)) / NTH;
-  const int kc = tid % KCH;
-  const int kb = tid % UK;
-
-  const uint16_t* a_ptr[A_PER];
-  bool a_ok[A_PER];
   const uint16_t* Bexp = g.B + (RAGGED_K ? 0 : (int64_t)e * g.b_estride);
-  if constexpr (!RAGGED_K) {
+
+  // ------------------------------------------------------------------ DMA source pointers
+  // KM operand, instruction q: LDS block gi = wave*(R/64) + q holds rows 16*gi..16*gi+15; lane
+  // L fills physical chunk L%4 of row 16*gi + L/4 from logical chunk (L%4) ^ ((row >> 2) & 3).
+  // KN operand (C columns), instruction q: block gi = wave*(C/64) + q holds k rows
+  // (512/C)*gi ..; lane L fills physical chunk L % (C/8) of k row (512/C)*gi + L/(C/8).
+  const uint16_t* a_src[QA];
+  const uint16_t* b_src[QB];
+  int a_kr[QA], b_kr[QB];  // KN: k row within the tile; KM: unused
+  int a_col[QA], b_col[QB];  // KN: global column offset of the lane's chunk
+  if constexpr (!A_KN) {
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int r = tid / KCH + i * (NTH / KCH);
-      a_ok[i] = r < mrows;
-      const int pos = m0 + (a_ok[i] ? r : 0);  // rows past the expert's end read row m0, then mask
+    for (int q = 0; q < QA; ++q) {
+      const int row = 16 * (wave * QA + q) + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      // rows past the expert's end read row m0: they only feed accumulator rows the epilogue
+      // never stores (an output row depends on its own A row only)
+      const int pos = m0 + (row < mrows ? row : 0);
       const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
-      a_ptr[i] = g.A + src * g.lda + kc * 8;
+      a_src[q] = g.A + src * g.lda + 8 * c;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      constexpr int CH = BM / 8;
+      a_kr[q] = (512 / BM) * (wave * QA + q) + lane / CH;
+      const int c = (lane % CH) ^ (4 * (a_kr[q] & 3));
+      a_col[q] = m0 + 8 * c;
     }
   }
-  // K-contiguous B rows n0 + tid/KCH + i*(NTH/KCH): one base pointer and a fixed row step
-  const uint16_t* b_base = Bexp + (int64_t)(n0 + tid / KCH) * g.ldb + kc * 8;
-  const int64_t b_step = (int64_t)(NTH / KCH) * g.ldb;
-  // global column of LDS row n for the K-strided B operand (UP pairs gate and up columns)
-  auto b_col = [&](int n) __attribute__((always_inline)) -> int {
-    if constexpr (MODE == M_UP) return n < BN / 2 ? n0 + n : g.f + n0 + (n - BN / 2);
-    else return n0 + n;
-  };
+  if constexpr (!B_KN) {
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int row = 16 * (wave * QB + q) + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      b_src[q] = Bexp + (int64_t)(n0 + row) * g.ldb + 8 * c;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      constexpr int CH = BN / 8;
+      b_kr[q] = (512 / BN) * (wave * QB + q) + lane / CH;
+      const int c = (lane % CH) ^ (4 * (b_kr[q] & 3));
+      int col;
+      if constexpr (MODE == M_UP) col = c < CH / 2 ? n0 + 8 * c : g.f + n0 + 8 * (c - CH / 2);
+      else col = n0 + 8 * c;
+      b_col[q] = col;
+      if constexpr (!RAGGED_K) b_src[q] = Bexp + (int64_t)b_kr[q] * g.ldb + col;
+    }
+  }
 
-  constexpr int NA = RAGGED_K ? 4 * A_UNITS : A_PER;
-  constexpr int NB = B_KC ? B_PER : 4 * B_UNITS;
-  u32x4 a_buf[NA];
-  u32x4 b_buf[NB];
-
-  auto load_tiles = [&](int k0) __attribute__((always_inline)) {
+  // Ragged K: a wave's DMA covers the 8 consecutive k rows 8*wave..8*wave+7 of the tile.  Their
+  // token rows come from one scalar load (tokrow[pos] = perm[pos] / k); rows past kend read the
+  // expert's first row and their A values are zeroed in LDS before use.
+  const int klen = kend - kbeg;
+  int tok_first = 0;
+  if constexpr (RAGGED_K)
+    if (klen > 0 && (g.gatherA || g.gatherB)) tok_first = ((const CONST_AS int32_t*)g.tokrow)[kbeg];
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    const int k0 = t * BK;
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES;
     if constexpr (!RAGGED_K) {
 #pragma unroll
-      for (int i = 0; i < A_PER; ++i) {
-        a_buf[i] = keep_if(*(const u32x4*)(a_ptr[i] + k0), a_ok[i]);
-      }
-      if constexpr (B_KC) {
+      for (int q = 0; q < QA; ++q) dma16(a_src[q] + k0, abase + (wave * QA + q) * 1024);
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i) b_buf[i] = *(const u32x4*)(b_base + i * b_step + k0);
-      } else {
-#pragma unroll
-        for (int u = 0; u < B_UNITS; ++u) {
-          const int cb = tid / UK + u * (NTH / UK);
-          const uint16_t* base = Bexp + (int64_t)(k0 + 4 * kb) * g.ldb + b_col(cb * 8);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) b_buf[4 * u + r] = *(const u32x4*)(base + (int64_t)r * g.ldb);
-        }
+      for (int q = 0; q < QB; ++q) {
+        const uint16_t* src = B_KN ? b_src[q] + (int64_t)k0 * g.ldb : b_src[q] + k0;
+        dma16(src, bbase + (wave * QB + q) * 1024);
       }
     } else {
-      // ragged K: rows pos = k0 + 4*kb + r of this expert, masked past kend
-      // rows past kend read the expert's first row (kbeg < kend whenever a tile is loaded), then mask
-      const uint16_t* arow[4];
-      const uint16_t* brow[4];
-      bool ok[4];
+      i32x8 tk;
+      if (g.gatherA || g.gatherB) tk = *(const CONST_AS i32x8*)(g.tokrow + kbeg + k0 + 8 * wave);
+      auto row_of = [&](int kr, bool gather) __attribute__((always_inline)) -> int64_t {
+        const int lk = kr - 8 * wave;  // 0..7
+        const bool ok = k0 + kr < klen;
+        if (!gather) return ok ? (int64_t)(kbeg + k0 + kr) : (int64_t)kbeg;
+        int t8 = tk[0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p0 = k0 + 4 * kb + r;
-        ok[r] = p0 < kend;
-        const int pos = ok[r] ? p0 : kbeg;
-        const int tok = g.perm[pos] / g.kslots;
-        arow[r] = g.A + (int64_t)(g.gatherA ? tok : pos) * g.lda;
-        brow[r] = g.B + (int64_t)(g.gatherB ? tok : pos) * g.ldb;
-      }
+        for (int z = 1; z < 8; ++z) t8 = (lk == z) ? tk[z] : t8;
+        return ok ? (int64_t)t8 : (int64_t)tok_first;
+      };
 #pragma unroll
-      for (int u = 0; u < A_UNITS; ++u) {
-        const int cb = tid / UK + u * (NTH / UK);
+      for (int q = 0; q < QA; ++q)
+        dma16(g.A + row_of(a_kr[q], g.gatherA) * g.lda + a_col[q], abase + (wave * QA + q) * 1024);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          a_buf[4 * u + r] = keep_if(*(const u32x4*)(arow[r] + m0 + cb * 8), ok[r]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < B_UNITS; ++u) {
-        const int cb = tid / UK + u * (NTH / UK);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          b_buf[4 * u + r] = keep_if(*(const u32x4*)(brow[r] + n0 + cb * 8), ok[r]);
-        }
-      }
+      for (int q = 0; q < QB; ++q)
+        dma16(g.B + row_of(b_kr[q], g.gatherB) * g.ldb + b_col[q], bbase + (wave * QB + q) * 1024);
     }
   };
 
-  auto store_tiles = [&](int buf) __attribute__((always_inline)) {
-    uint16_t* la = sA[buf];
-    uint16_t* lb = sB[buf];
-    if constexpr (!RAGGED_K) {
-#pragma unroll
-      for (int i = 0; i < A_PER; ++i) {
-        const int r = tid / KCH + i * (NTH / KCH);
-        *(u32x4*)&la[r * BK + ((kc ^ (r % KCH)) * 8)] = a_buf[i];
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < A_UNITS; ++u)
-        store_transposed<BK>(la, (tid / UK + u * (NTH / UK)) * 8, kb, a_buf[4 * u], a_buf[4 * u + 1], a_buf[4 * u + 2],
-                             a_buf[4 * u + 3]);
-    }
-    if constexpr (B_KC) {
-#pragma unroll
-      for (int i = 0; i < B_PER; ++i) {
-        const int r = tid / KCH + i * (NTH / KCH);
-        *(u32x4*)&lb[r * BK + ((kc ^ (r % KCH)) * 8)] = b_buf[i];
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < B_UNITS; ++u)
-        store_transposed<BK>(lb, (tid / UK + u * (NTH / UK)) * 8, kb, b_buf[4 * u], b_buf[4 * u + 1], b_buf[4 * u + 2],
-                             b_buf[4 * u + 3]);
-    }
-  };
-
-  // LDS row of the wave's j-th 32-column B fragment
+  // LDS column of the wave's j-th 32-column B fragment
   auto b_row = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (MODE == M_UP)
       return j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32;
@@ -295,22 +301,20 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    const uint16_t* la = sA[buf];
-    const uint16_t* lb = sB[buf];
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = kk * 2 + (lane >> 5);
       bf16x8_t af[FM], bv[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int r = wm * TM + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8_t*)&la[r * BK + ((ch ^ (r % KCH)) * 8)];
+        if constexpr (A_KN) af[i] = read_kn<BM>(abase, wm * TM + i * 32, kk, lane);
+        else af[i] = read_km(abase, wm * TM + i * 32 + (lane & 31), 2 * kk + (lane >> 5));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int r = b_row(j) + (lane & 31);
-        bv[j] = *(const bf16x8_t*)&lb[r * BK + ((ch ^ (r % KCH)) * 8)];
+        if constexpr (B_KN) bv[j] = read_kn<BN>(bbase, b_row(j), kk, lane);
+        else bv[j] = read_km(bbase, b_row(j) + (lane & 31), 2 * kk + (lane >> 5));
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -321,19 +325,30 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
   };
 
   // ------------------------------------------------------------------ main loop
-  const int nk = (kend - kbeg + BK - 1) / BK;
-  if (nk > 0) {
-    load_tiles(kbeg);
-    store_tiles(0);
-    __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-      const int cur = it & 1;
-      const bool more = it + 1 < nk;
-      if (more) load_tiles(kbeg + (it + 1) * BK);
-      compute(cur);
-      if (more) store_tiles(cur ^ 1);
-      __syncthreads();
+  // Stage t%S holds tile t.  Iteration t: wait until tile t's DMA has landed (tiles t+1..t+S-2
+  // may stay in flight) and all waves are past tile t-1, refill tile t-1's stage with tile
+  // t+S-1, then run tile t's MFMAs.
+  const int nk = (klen + BK - 1) / BK;
+  __syncthreads();  // s_slot / s_w visible; the arena is free
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t)
+    if (t < nk) issue(t, t);
+  for (int it = 0; it < nk; ++it) {
+    const int pend = min(S - 2, nk - 1 - it);
+    if (pend >= 2) vm_wait_barrier<2 * DPT>();
+    else if (pend == 1) vm_wait_barrier<DPT>();
+    else vm_wait_barrier<0>();
+    if constexpr (RAGGED_K) {
+      const int kvalid = klen - it * BK;
+      if (kvalid < BK) {  // last tile of the expert: zero A's k rows past kend
+        uint8_t* a = smem + (it % S) * STAGE;
+        for (int z = kvalid * 2 * BM + tid * 16; z < A_BYTES; z += NTH * 16)
+          *(u32x4*)(a + z) = u32x4{0u, 0u, 0u, 0u};
+        lds_barrier();
+      }
     }
+    if (it + S - 1 < nk) issue(it + S - 1, (it + S - 1) % S);
+    compute(it % S);
   }
   __syncthreads();
 
@@ -450,7 +465,6 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
 
 // ---------------------------------------------------------------------- host launchers
 namespace {
-constexpr int BK = 64;
 
 // Launch MODE with a BM x BN tile: 256x256 (waves own 128x128, one block per CU) where the
 // output width allows, else 256x128 / 128x256 / 128x128.
@@ -458,13 +472,13 @@ template <int MODE>
 hipError_t run(const GemmArgs& g, int bm, int bn, dim3 grid, hipStream_t st) {
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   if (bm == 256 && bn == 256)
-    grouped_gemm_kernel<MODE, 256, 256, BK, 2, 2, 1><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 256, 256, 1><<<grid, 256, 0, st>>>(g);
   else if (bm == 256 && bn == 128)
-    grouped_gemm_kernel<MODE, 256, 128, BK, 2, 2, 1><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 256, 128, 1><<<grid, 256, 0, st>>>(g);
   else if (MODE == M_WG && bm == 128 && bn == 256)
-    grouped_gemm_kernel<MODE, 128, 256, BK, 2, 2, 1><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 128, 256, 1><<<grid, 256, 0, st>>>(g);
   else if (bm == 128 && bn == 128)
-    grouped_gemm_kernel<MODE, 128, 128, BK, 2, 2, 2><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 128, 128, 2><<<grid, 256, 0, st>>>(g);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -579,8 +593,9 @@ hipError_t launch_gemm_dx(const MoeShape& s, const uint16_t* dH, const uint16_t*
 }
 
 hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t* dy, const int32_t* offsets,
-                           const int32_t* perm, uint16_t* dW2, hipStream_t st) {
+                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW2, hipStream_t st) {
   GemmArgs g = base_args(s, offsets, perm, nullptr, nullptr);
+  g.tokrow = tokrow;
   g.A = As;
   g.lda = s.f;
   g.gatherA = 0;
@@ -597,8 +612,9 @@ hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t
 }
 
 hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t* dH, const int32_t* offsets,
-                           const int32_t* perm, uint16_t* dW1, hipStream_t st) {
+                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW1, hipStream_t st) {
   GemmArgs g = base_args(s, offsets, perm, nullptr, nullptr);
+  g.tokrow = tokrow;
   g.A = x;
   g.lda = s.d;
   g.gatherA = 1;

@@ -44,10 +44,14 @@ hipError_t launch_gemm_dx(const MoeShape& s, const uint16_t* dH, const uint16_t*
                           hipStream_t st);
 // Weight gradients (ragged K = the expert's rows):
 //   dW2[e] = As_e^T . dy[perm/k]_e     dW1[e] = x[perm/k]_e^T . dH_e
+//   tokrow[pos] = perm[pos] / k for pos < offsets[E], padded by kTokrowPad readable entries.
 hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t* dy, const int32_t* offsets,
-                           const int32_t* perm, uint16_t* dW2, hipStream_t st);
+                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW2, hipStream_t st);
 hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t* dH, const int32_t* offsets,
-                           const int32_t* perm, uint16_t* dW1, hipStream_t st);
+                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW1, hipStream_t st);
+constexpr int kTokrowPad = 64;
+hipError_t launch_tokrow(const int32_t* perm, const int32_t* offsets, int E, int64_t A, int k, int32_t* tokrow,
+                         hipStream_t st);
 
 // data movement and router backward
 hipError_t launch_permute(const uint16_t* x, const int32_t* perm, const int32_t* offsets, int64_t A, int d, int k,

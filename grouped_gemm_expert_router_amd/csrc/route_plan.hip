@@ -281,4 +281,22 @@ hipError_t launch_tile_map(const int32_t* offsets, int E, int BM, int2* tiles, i
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------ token rows
+// tokrow[pos] = perm[pos] / k for routed positions; every other entry (unrouted tail and the
+// padding the weight-gradient GEMMs may read past an expert's last row) is 0, a valid row.
+__global__ __launch_bounds__(256) void tokrow_kernel(const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ total, int64_t n, int k,
+                                                     int32_t* __restrict__ tokrow) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  tokrow[i] = (i < *total) ? perm[i] / k : 0;
+}
+
+hipError_t launch_tokrow(const int32_t* perm, const int32_t* offsets, int E, int64_t A, int k, int32_t* tokrow,
+                         hipStream_t st) {
+  const int64_t n = A + kTokrowPad;
+  tokrow_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, offsets + E, n, k, tokrow);
+  return hipGetLastError();
+}
+
 }  // namespace moe
