@@ -91,6 +91,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 #define CONST_AS __attribute__((address_space(4)))
 
@@ -100,20 +101,26 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 
 // Operand tiles in LDS (16-byte chunks, XOR-swizzled so the 16 lanes an LDS cycle serves hit
 // 16 distinct 16-byte bank groups of the 64-bank LDS):
-//   KM: [row][BK=32] for K-contiguous sources; row = 64 bytes = 4 chunks; chunk c of row r
-//       lives at chunk c ^ ((r >> 2) & 3).  MFMA operand = one ds_read_b128.
+//   KM: [row][BK] for K-contiguous sources.  BK = 32: row = 64 bytes = 4 chunks, chunk c of
+//       row r lives at chunk c ^ ((r >> 2) & 3); BK = 64: row = 128 bytes = 8 chunks, chunk c
+//       at c ^ ((r >> 1) & 7).  MFMA operand = one ds_read_b128.
 //   KN: [k][C] for sources contiguous along M or N; k row = 2C bytes; chunk c of k row r lives
 //       at chunk c ^ (4 * (r & 3)).  MFMA operand = two ds_read_b64_tr_b16: within a 16-lane
 //       group, lane s supplies the address of (k = k0 + s/4, col = c0 + 4*(s%4)) and lane i
 //       receives the 4 values (k0..k0+3, c0 + i).
-__device__ __forceinline__ uint32_t km_off(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+template <int BK>
+__device__ __forceinline__ uint32_t km_off(int row, int c) {
+  if constexpr (BK == 32) return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
+  else return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+}
 template <int C>
 __device__ __forceinline__ uint32_t kn_off(int kr, int col) {
   return kr * (2 * C) + ((((col >> 3) ^ (4 * (kr & 3)))) << 4) + ((col & 7) << 1);
 }
 
+template <int BK>
 __device__ __forceinline__ bf16x8_t read_km(uint32_t base, int row, int c) {
-  return *(const LDS_AS bf16x8_t*)(uintptr_t)(base + km_off(row, c));
+  return *(const LDS_AS bf16x8_t*)(uintptr_t)(base + km_off<BK>(row, c));
 }
 // 32-column fragment at column cbase, k16 step kk: lane holds column cbase + lane%32 and
 // k = 16*kk + 8*(lane/32) + 0..7.
@@ -129,18 +136,20 @@ __device__ __forceinline__ bf16x8_t read_kn(uint32_t base, int cbase, int kk, in
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int MODE, int BM, int BN, int OCC>
-__global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g) {
-  constexpr int NTH = 256, BK = 32, S = 4, WM = 2, WN = 2;
+template <int MODE, int BM, int BN, int WN, int OCC, int BK>
+__global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmArgs g) {
+  constexpr int S = BK == 32 ? 4 : 2, WM = 2, NW = WM * WN, NTH = 64 * NW;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr bool RAGGED_K = (MODE == M_WG);
   constexpr bool A_KN = RAGGED_K;                              // A stored [k][m]
   constexpr bool B_KN = !(MODE == M_DACT || MODE == M_DX);     // B stored [k][n]
   static_assert(MODE != M_UP || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
-  constexpr int QA = BM / 64, QB = BN / 64;  // DMA instructions per thread per tile
+  constexpr int QA = BM * BK / (512 * NW), QB = BN * BK / (512 * NW);  // DMA instrs per thread per tile
+  constexpr int KRW = BK / NW;                                 // ragged K: k rows per wave's DMA
+  static_assert(QA >= 1 && QB >= 1 && (!RAGGED_K || KRW == 4 || KRW == 8), "tile / wave split");
   constexpr int DPT = QA + QB;
-  static_assert(DPT * (S - 2) <= 63, "vmcnt range");
+  static_assert(DPT * (S - 2) <= 63 && (BK == 32 || BK == 64), "vmcnt range");
 
   // One LDS arena: S operand stages during the K loop, then the fp32 staging band of the
   // epilogue (64 rows x BN columns, rows padded by 4 floats against bank conflicts).
@@ -208,8 +217,9 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
   if constexpr (!A_KN) {
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-      const int row = 16 * (wave * QA + q) + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      constexpr int CPR = BK / 8;  // 16-byte chunks per row
+      const int row = (64 / CPR) * (wave * QA + q) + lane / CPR;
+      const int c = (lane % CPR) ^ (BK == 32 ? ((row >> 2) & 3) : ((row >> 1) & 7));
       // rows past the expert's end read row m0: they only feed accumulator rows the epilogue
       // never stores (an output row depends on its own A row only)
       const int pos = m0 + (row < mrows ? row : 0);
@@ -228,8 +238,9 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
   if constexpr (!B_KN) {
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      const int row = 16 * (wave * QB + q) + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      constexpr int CPR = BK / 8;
+      const int row = (64 / CPR) * (wave * QB + q) + lane / CPR;
+      const int c = (lane % CPR) ^ (BK == 32 ? ((row >> 2) & 3) : ((row >> 1) & 7));
       b_src[q] = Bexp + (int64_t)(n0 + row) * g.ldb + 8 * c;
     }
   } else {
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
     }
   }
 
-  // Ragged K: a wave's DMA covers the 8 consecutive k rows 8*wave..8*wave+7 of the tile.  Their
+  // Ragged K: a wave's DMA covers the KRW consecutive k rows KRW*wave.. of the tile.  Their
   // token rows come from one scalar load (tokrow[pos] = perm[pos] / k); rows past kend read the
   // expert's first row and their A values are zeroed in LDS before use.
   const int klen = kend - kbeg;
@@ -265,15 +276,25 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
         dma16(src, bbase + (wave * QB + q) * 1024);
       }
     } else {
-      i32x8 tk;
-      if (g.gatherA || g.gatherB) tk = *(const CONST_AS i32x8*)(g.tokrow + kbeg + k0 + 8 * wave);
+      int tk[KRW];
+      if (g.gatherA || g.gatherB) {
+        if constexpr (KRW == 8) {
+          const i32x8 v = *(const CONST_AS i32x8*)(g.tokrow + kbeg + k0 + KRW * wave);
+#pragma unroll
+          for (int z = 0; z < 8; ++z) tk[z] = v[z];
+        } else {
+          const i32x4 v = *(const CONST_AS i32x4*)(g.tokrow + kbeg + k0 + KRW * wave);
+#pragma unroll
+          for (int z = 0; z < 4; ++z) tk[z] = v[z];
+        }
+      }
       auto row_of = [&](int kr, bool gather) __attribute__((always_inline)) -> int64_t {
-        const int lk = kr - 8 * wave;  // 0..7
+        const int lk = kr - KRW * wave;  // 0..KRW-1
         const bool ok = k0 + kr < klen;
         if (!gather) return ok ? (int64_t)(kbeg + k0 + kr) : (int64_t)kbeg;
         int t8 = tk[0];
 #pragma unroll
-        for (int z = 1; z < 8; ++z) t8 = (lk == z) ? tk[z] : t8;
+        for (int z = 1; z < KRW; ++z) t8 = (lk == z) ? tk[z] : t8;
         return ok ? (int64_t)t8 : (int64_t)tok_first;
       };
 #pragma unroll
@@ -309,12 +330,12 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         if constexpr (A_KN) af[i] = read_kn<BM>(abase, wm * TM + i * 32, kk, lane);
-        else af[i] = read_km(abase, wm * TM + i * 32 + (lane & 31), 2 * kk + (lane >> 5));
+        else af[i] = read_km<BK>(abase, wm * TM + i * 32 + (lane & 31), 2 * kk + (lane >> 5));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if constexpr (B_KN) bv[j] = read_kn<BN>(bbase, b_row(j), kk, lane);
-        else bv[j] = read_km(bbase, b_row(j) + (lane & 31), 2 * kk + (lane >> 5));
+        else bv[j] = read_km<BK>(bbase, b_row(j) + (lane & 31), 2 * kk + (lane >> 5));
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -335,8 +356,8 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(const GemmArgs g
     if (t < nk) issue(t, t);
   for (int it = 0; it < nk; ++it) {
     const int pend = min(S - 2, nk - 1 - it);
-    if (pend >= 2) vm_wait_barrier<2 * DPT>();
-    else if (pend == 1) vm_wait_barrier<DPT>();
+    if (S >= 4 && pend >= 2) vm_wait_barrier<(S >= 4 ? 2 : 0) * DPT>();
+    else if (S >= 3 && pend == 1) vm_wait_barrier<(S >= 3 ? 1 : 0) * DPT>();
     else vm_wait_barrier<0>();
     if constexpr (RAGGED_K) {
       const int kvalid = klen - it * BK;
@@ -468,17 +489,24 @@ namespace {
 
 // Launch MODE with a BM x BN tile: 256x256 (waves own 128x128, one block per CU) where the
 // output width allows, else 256x128 / 128x256 / 128x128.
+// Tile configs: 256x256 and 256x128 run 8 waves (2 per SIMD, each owning 128x64 or 128x32)
+// so one wave's MFMAs cover the other's LDS and barrier waits; 128x128 runs 4 waves.  K step
+// per LDS stage: BK = 32 with 4 stages or BK = 64 with 2 stages (GEMM_BK below).
+#ifndef GEMM_BK
+#define GEMM_BK 64
+#endif
 template <int MODE>
 hipError_t run(const GemmArgs& g, int bm, int bn, dim3 grid, hipStream_t st) {
+  constexpr int BKC = GEMM_BK;
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   if (bm == 256 && bn == 256)
-    grouped_gemm_kernel<MODE, 256, 256, 1><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 256, 256, 4, 1, BKC><<<grid, 512, 0, st>>>(g);
   else if (bm == 256 && bn == 128)
-    grouped_gemm_kernel<MODE, 256, 128, 1><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 256, 128, (MODE == M_UP ? 2 : 4), 1, BKC><<<grid, (MODE == M_UP ? 256 : 512), 0, st>>>(g);
   else if (MODE == M_WG && bm == 128 && bn == 256)
-    grouped_gemm_kernel<MODE, 128, 256, 1><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 128, 256, 4, 1, BKC><<<grid, 512, 0, st>>>(g);
   else if (bm == 128 && bn == 128)
-    grouped_gemm_kernel<MODE, 128, 128, 2><<<grid, 256, 0, st>>>(g);
+    grouped_gemm_kernel<MODE, 128, 128, 2, 2, 32><<<grid, 256, 0, st>>>(g);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
