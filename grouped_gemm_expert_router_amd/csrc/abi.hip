@@ -40,7 +40,8 @@ struct FwdLayout {
   size_t tiles, ntiles, op, total;
 };
 struct BwdLayout {
-  size_t tiles, ntiles, tokrow, dH, dXp, dwp, total;
+  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, total;
+  int max_partials;
 };
 struct SavedLayout {
   size_t H, As, total;
@@ -76,8 +77,28 @@ BwdLayout bwd_layout(const moe_dims* d) {
   off += al256((size_t)A * d->d * 2);
   L.dwp = off;
   off += al256((size_t)A * (d->f / dact_bn((int)d->f)) * sizeof(float));
+  L.max_partials = wg_max_partials(shape_of(d));
+  L.wg_units = off;
+  off += al256((size_t)(d->E + L.max_partials) * sizeof(int2));
+  L.wg_meta = off;
+  off += 256;
+  L.wg_pslot = off;
+  off += al256((size_t)d->E * sizeof(int32_t));
+  L.wg_partial = off;
+  off += al256((size_t)L.max_partials * d->d * 2 * d->f * sizeof(float));
   L.total = off;
   return L;
+}
+
+WgSplit wg_split_of(const BwdLayout& L, char* w, const int32_t* offsets) {
+  WgSplit sp;
+  sp.units = (int2*)(w + L.wg_units);
+  sp.meta = (int32_t*)(w + L.wg_meta);
+  sp.pslot = (int32_t*)(w + L.wg_pslot);
+  sp.partial = (float*)(w + L.wg_partial);
+  sp.offsets = offsets;
+  sp.max_partials = L.max_partials;
+  return sp;
 }
 
 SavedLayout saved_layout(const moe_dims* d) {
@@ -210,13 +231,16 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   if (x_scale || W1_scale || W2_scale) return MOE_ERR_DTYPE;
   if (dims->T == 0) {
     // no routed pair: every expert's weight gradient is exactly zero, nothing else to write
-    if (!offsets || !dW1 || !dW2) return MOE_ERR_NULL;
-    if (!al16(dW1) || !al16(dW2)) return MOE_ERR_ALIGN;
+    if (!offsets || !dW1 || !dW2 || !ws) return MOE_ERR_NULL;
+    const BwdLayout L0 = bwd_layout(dims);
+    if (ws_bytes < L0.total) return MOE_ERR_WORKSPACE;
+    if (!al16(dW1) || !al16(dW2) || !al256p(ws)) return MOE_ERR_ALIGN;
     const MoeShape s = shape_of(dims);
     hipStream_t st = (hipStream_t)stream;
-    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, nullptr, nullptr, offsets, nullptr, nullptr, (uint16_t*)dW2, st));
-    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, nullptr, nullptr, offsets, nullptr, nullptr, (uint16_t*)dW1, st));
-
+    const WgSplit sp = wg_split_of(L0, (char*)ws, offsets);
+    MOE_TRY("wg_split", launch_wg_split(s, offsets, sp, st));
+    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, nullptr, nullptr, offsets, nullptr, nullptr, sp, (uint16_t*)dW2, st));
+    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, nullptr, nullptr, offsets, nullptr, nullptr, sp, (uint16_t*)dW1, st));
     return MOE_OK;
   }
   if (!dy || !x || !W1 || !W2 || !topk_w || !offsets || !perm || !inv_perm || !saved || !dx || !dW1 || !dW2 ||
@@ -246,9 +270,13 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                            dwp, st));
   MOE_TRY("gemm_dx", launch_gemm_dx(s, dH, (const uint16_t*)W1, offsets, perm, tiles, ntiles, dXp, st));
   MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
+  const WgSplit sp = wg_split_of(L, w, offsets);
   MOE_TRY("tokrow", launch_tokrow(perm, offsets, s.E, (int64_t)s.T * s.k, s.k, tokrow, st));
-  MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, (uint16_t*)dW2, st));
-  MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, tokrow, (uint16_t*)dW1, st));
+  MOE_TRY("wg_split", launch_wg_split(s, offsets, sp, st));
+  MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, sp, (uint16_t*)dW2, st));
+  MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.f * s.d, (uint16_t*)dW2, st));
+  MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, tokrow, sp, (uint16_t*)dW1, st));
+  MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.d * 2 * s.f, (uint16_t*)dW1, st));
   MOE_TRY("dlogits", launch_dlogits(dwp, s.f / dact_bn(s.f), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
                                    st));
 

@@ -51,6 +51,12 @@ struct GemmArgs {
   int64_t ldh;
   float* dwp;
   int nparts;
+  // ragged K split: work unit u = (expert, chunk) of KC rows; experts split into several chunks
+  // write fp32 partials (slot wg_pslot[e] + chunk) that a second kernel sums in chunk order
+  const int2* wg_units;
+  const int32_t* wg_meta;   // [0] units, [1] KC
+  const int32_t* wg_pslot;  // first partial slot of a split expert, -1 if not split
+  float* partial;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -167,24 +173,47 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
 
   // ------------------------------------------------------------------ tile coordinates
+  // The grid is sized for the worst case; only the first G_valid blocks (known on the device)
+  // have work.  They are spread round-robin over the XCDs, so remapping within G_valid keeps
+  // every XCD equally busy.
   int e, m0, mrows, n0, nt, kbeg, kend;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  int kchunk = 0, pslot = -1;
   if constexpr (RAGGED_K) {
     const int nN = g.N / BN;
-    const int per_e = (g.Mo / BM) * nN;
-    e = lid / per_e;
-    nt = (lid % per_e) % nN;
-    m0 = ((lid % per_e) / nN) * BM;
+    const int per_u = (g.Mo / BM) * nN;
+    const CONST_AS int32_t* meta = (const CONST_AS int32_t*)g.wg_meta;
+    const int G_valid = meta[0] * per_u;
+    if ((int)blockIdx.x >= G_valid) return;  // uniform: the block has no work
+    // Units are in decreasing size and blocks go round-robin to the XCDs, so every XCD gets an
+    // equal share of each unit; within a unit the dimension with 8 tiles runs fastest, so an
+    // XCD's share of a unit reuses one operand slice.
+    const int lid = blockIdx.x;
+    const int u = lid / per_u;
+    const CONST_AS int32_t* up = (const CONST_AS int32_t*)g.wg_units;
+    e = up[2 * u];
+    kchunk = up[2 * u + 1];
+    const int t = lid % per_u, nM = g.Mo / BM;
+    if (nM % 8 == 0 || nN % 8 != 0) {
+      m0 = (t % nM) * BM;
+      nt = t / nM;
+    } else {
+      nt = t % nN;
+      m0 = (t / nN) * BM;
+    }
     mrows = BM;
     n0 = nt * BN;
     const CONST_AS int32_t* off4 = (const CONST_AS int32_t*)g.offsets;
-    kbeg = off4[e];
-    kend = off4[e + 1];
+    const int KC = meta[1];
+    kbeg = off4[e] + kchunk * KC;
+    kend = min(off4[e + 1], kbeg + KC);
+    pslot = ((const CONST_AS int32_t*)g.wg_pslot)[e];
   } else {
     const int nN = (MODE == M_UP) ? g.f / (BN / 2) : g.N / BN;
+    const int G_valid = *(const CONST_AS int32_t*)g.ntiles * nN;
+    if ((int)blockIdx.x >= G_valid) return;  // uniform: the block has no work
+    const int lid = xcd_remap(blockIdx.x, G_valid);
     nt = lid % nN;
     const int tile = lid / nN;
-    if (tile >= *g.ntiles) return;  // uniform: the block has no work
     const int2 te = g.tiles[tile];
     e = te.x;
     m0 = g.offsets[e] + te.y * BM;
@@ -464,6 +493,17 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
         for (int m = CH / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
         if (ok && cc == 0) g.dwp[(int64_t)(m0 + lr) * g.nparts + nt] = part;
       }
+    } else if (MODE == M_WG && pslot >= 0) {
+      // one chunk of a split expert: fp32 partial, summed later in chunk order
+      float* out = g.partial + (int64_t)(pslot + kchunk) * g.Mo * g.N;
+      for (int id = tid; id < 64 * CH; id += NTH) {
+        const int q = id / CH, cc = id % CH;
+        const int lr = tile_row(q);
+        const float* cp = &cband[q * CPAD + cc * 8];
+        float* o = out + (int64_t)(m0 + lr) * g.N + n0 + cc * 8;
+        *(float4*)o = make_float4(cp[0], cp[1], cp[2], cp[3]);
+        *(float4*)(o + 4) = make_float4(cp[4], cp[5], cp[6], cp[7]);
+      }
     } else {
       // plain bf16 store: DOWN/DX rows go to the pair's slot, WG rows to dW[e]
       for (int id = tid; id < 64 * CH; id += NTH) {
@@ -620,10 +660,112 @@ hipError_t launch_gemm_dx(const MoeShape& s, const uint16_t* dH, const uint16_t*
   return run<M_DX>(g, kGemmBM, bn, grid, st);
 }
 
+// ------------------------------------------------------------------ weight-gradient split
+// One block: per expert e with c rows, nchunks = ceil(c / KC) if c > KC else 1 (an empty expert
+// still gets one unit, which writes its zero gradient).  KC starts at kWgChunk and doubles until
+// the split experts' chunks fit the max_partials fp32 slots.
+__global__ __launch_bounds__(1024) void wg_split_kernel(const int32_t* __restrict__ offsets, int E, int kc_min,
+                                                        int max_partials, int2* __restrict__ units,
+                                                        int32_t* __restrict__ meta, int32_t* __restrict__ pslot) {
+  __shared__ int sh[64];
+  __shared__ int s_flag;
+  const int e = threadIdx.x;
+  const int c = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+  int KC = kc_min;
+  if (max_partials < 2) KC = 0x40000000;  // no room for partials: never split
+  for (;;) {
+    const int need = (max_partials >= 2 && e < E && c > KC) ? (c + KC - 1) / KC : 0;
+    int ex;
+    const int tot = block_excl_scan_1024(need, sh, &ex);
+    if (tot <= max_partials || KC >= 0x40000000) break;
+    KC *= 2;
+  }
+  const bool split = max_partials >= 2 && e < E && c > KC;
+  const int nch = (e < E) ? (split ? (c + KC - 1) / KC : 1) : 0;
+  int pbase, ubase;
+  block_excl_scan_1024(split ? nch : 0, sh, &pbase);
+  const int total = block_excl_scan_1024(nch, sh, &ubase);
+  // Unit list in expert order, with each unit's row count, staged in LDS; then written out
+  // largest first (ties by position), so the long units start first and the hardware's
+  // round-robin over XCDs spreads them evenly.
+  __shared__ int2 s_unit[2048];
+  __shared__ int s_rows[2048];
+  if (e < E) {
+    pslot[e] = split ? pbase : -1;
+    for (int ch = 0; ch < nch; ++ch) {
+      s_unit[ubase + ch] = make_int2(e, ch);
+      s_rows[ubase + ch] = min(KC, c - ch * KC);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < total; i += 1024) {
+    const int ri = s_rows[i];
+    int rank = 0;
+    for (int j = 0; j < total; ++j) {
+      const int rj = s_rows[j];
+      rank += (rj > ri) || (rj == ri && j < i);
+    }
+    units[rank] = s_unit[i];
+  }
+  if (e == 0) {
+    meta[0] = total;
+    meta[1] = KC;
+  }
+  (void)s_flag;
+}
+
+// dW[e] = bf16(sum over chunks, in chunk order, of the fp32 partials) for split experts.
+__global__ __launch_bounds__(256) void wg_reduce_kernel(const float* __restrict__ partial,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ meta,
+                                                        const int32_t* __restrict__ pslot, int64_t per_e,
+                                                        uint16_t* __restrict__ dW) {
+  const int e = blockIdx.y;
+  const int ps = pslot[e];
+  if (ps < 0) return;
+  const int KC = meta[1];
+  const int c = offsets[e + 1] - offsets[e];
+  const int nch = (c + KC - 1) / KC;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < per_e; i += (int64_t)gridDim.x * 256 * 8) {
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int ch = 0; ch < nch; ++ch) {
+      const float* p = partial + (int64_t)(ps + ch) * per_e + i;
+      const float4 u = *(const float4*)p, v = *(const float4*)(p + 4);
+      a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
+      a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+    }
+    *(uint4*)&dW[(int64_t)e * per_e + i] = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                      pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
+  }
+}
+
+int wg_max_partials(const MoeShape& s) {
+  const int64_t per = (int64_t)s.d * 2 * s.f * 4;  // the larger of dW1 / dW2, in fp32
+  int64_t p = kWgPartialBudget / per;
+  if (p > kWgMaxPartials) p = kWgMaxPartials;
+  return p < 2 ? 0 : (int)p;
+}
+
+hipError_t launch_wg_split(const MoeShape& s, const int32_t* offsets, const WgSplit& sp, hipStream_t st) {
+  wg_split_kernel<<<1, 1024, 0, st>>>(offsets, s.E, kWgChunk, sp.max_partials, sp.units, sp.meta, sp.pslot);
+  return hipGetLastError();
+}
+
+hipError_t launch_wg_reduce(const MoeShape& s, const WgSplit& sp, int64_t per_e, uint16_t* dW, hipStream_t st) {
+  if (sp.max_partials == 0) return hipSuccess;
+  dim3 grid(64, s.E);
+  wg_reduce_kernel<<<grid, 256, 0, st>>>(sp.partial, sp.offsets, sp.meta, sp.pslot, per_e, dW);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t* dy, const int32_t* offsets,
-                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW2, hipStream_t st) {
+                           const int32_t* perm, const int32_t* tokrow, const WgSplit& sp, uint16_t* dW2, hipStream_t st) {
   GemmArgs g = base_args(s, offsets, perm, nullptr, nullptr);
   g.tokrow = tokrow;
+  g.wg_units = sp.units;
+  g.wg_meta = sp.meta;
+  g.wg_pslot = sp.pslot;
+  g.partial = sp.partial;
   g.A = As;
   g.lda = s.f;
   g.gatherA = 0;
@@ -635,14 +777,18 @@ hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t
   g.C0 = dW2;
   g.ldc0 = s.d;
   const int bm = pick_bn(s.f), bn = pick_bn(s.d);
-  dim3 grid((unsigned)((s.f / bm) * (s.d / bn) * s.E));
+  dim3 grid((unsigned)((s.f / bm) * (s.d / bn) * (s.E + sp.max_partials)));
   return run<M_WG>(g, bm, bn, grid, st);
 }
 
 hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t* dH, const int32_t* offsets,
-                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW1, hipStream_t st) {
+                           const int32_t* perm, const int32_t* tokrow, const WgSplit& sp, uint16_t* dW1, hipStream_t st) {
   GemmArgs g = base_args(s, offsets, perm, nullptr, nullptr);
   g.tokrow = tokrow;
+  g.wg_units = sp.units;
+  g.wg_meta = sp.meta;
+  g.wg_pslot = sp.pslot;
+  g.partial = sp.partial;
   g.A = x;
   g.lda = s.d;
   g.gatherA = 1;
@@ -654,7 +800,7 @@ hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t*
   g.C0 = dW1;
   g.ldc0 = 2 * (int64_t)s.f;
   const int bm = pick_bn(s.d), bn = pick_bn(2 * s.f);
-  dim3 grid((unsigned)((s.d / bm) * (2 * s.f / bn) * s.E));
+  dim3 grid((unsigned)((s.d / bm) * (2 * s.f / bn) * (s.E + sp.max_partials)));
   return run<M_WG>(g, bm, bn, grid, st);
 }
 

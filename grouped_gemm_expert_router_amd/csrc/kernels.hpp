@@ -45,10 +45,28 @@ hipError_t launch_gemm_dx(const MoeShape& s, const uint16_t* dH, const uint16_t*
 // Weight gradients (ragged K = the expert's rows):
 //   dW2[e] = As_e^T . dy[perm/k]_e     dW1[e] = x[perm/k]_e^T . dH_e
 //   tokrow[pos] = perm[pos] / k for pos < offsets[E], padded by kTokrowPad readable entries.
+// Experts with more than KC rows (KC >= kWgChunk, chosen on the device) are split into chunks
+// whose fp32 partials (at most max_partials slots) are summed in chunk order by launch_wg_reduce.
+constexpr int kWgChunk = 2048;
+constexpr int kWgMaxPartials = 32;
+constexpr int64_t kWgPartialBudget = (int64_t)512 << 20;
+struct WgSplit {
+  int2* units;       // [E + max_partials]
+  int32_t* meta;     // [2]
+  int32_t* pslot;    // [E]
+  float* partial;    // [max_partials, max(d*2f, f*d)]
+  const int32_t* offsets;
+  int max_partials;
+};
+int wg_max_partials(const MoeShape& s);
+hipError_t launch_wg_split(const MoeShape& s, const int32_t* offsets, const WgSplit& sp, hipStream_t st);
+hipError_t launch_wg_reduce(const MoeShape& s, const WgSplit& sp, int64_t per_e, uint16_t* dW, hipStream_t st);
 hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t* dy, const int32_t* offsets,
-                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW2, hipStream_t st);
+                           const int32_t* perm, const int32_t* tokrow, const WgSplit& sp, uint16_t* dW2,
+                           hipStream_t st);
 hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t* dH, const int32_t* offsets,
-                           const int32_t* perm, const int32_t* tokrow, uint16_t* dW1, hipStream_t st);
+                           const int32_t* perm, const int32_t* tokrow, const WgSplit& sp, uint16_t* dW1,
+                           hipStream_t st);
 constexpr int kTokrowPad = 64;
 hipError_t launch_tokrow(const int32_t* perm, const int32_t* offsets, int E, int64_t A, int k, int32_t* tokrow,
                          hipStream_t st);

@@ -132,34 +132,6 @@ __global__ __launch_bounds__(256) void plan_hist_kernel(const int32_t* __restric
     for (int e = lane; e < E; e += 64) segcnt[(size_t)e * S + s] = cnt[e];
 }
 
-// Exclusive scan of one int per thread over a 1024-thread block; returns the block total.
-__device__ int block_excl_scan_1024(int v, int* sh, int* excl) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wv] = x;
-  __syncthreads();
-  if (wv == 0) {
-    int t = (lane < 16) ? sh[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(t, o, 64);
-      if (lane >= o) t += y;
-    }
-    if (lane < 16) sh[16 + lane] = t;  // inclusive wave totals
-  }
-  __syncthreads();
-  const int before = (wv == 0) ? 0 : sh[16 + wv - 1];
-  *excl = before + x - v;
-  const int total = sh[16 + 15];
-  __syncthreads();
-  return total;
-}
-
 __global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restrict__ segcnt, int E, int S,
                                                          int32_t* __restrict__ segbase,
                                                          int32_t* __restrict__ counts,

@@ -141,3 +141,18 @@ def test_permute_then_combine_is_k_times_x_bitexact(k):
     # the gather itself: sorted row pos holds token perm[pos] // k
     perm = b["perm"][:A].long()
     assert torch.equal(xp.view(torch.int16), gl.x[perm // k].view(torch.int16))
+
+
+@pytest.mark.parametrize("T,k", [(2600, 2), (5000, 1)])
+def test_weight_gradient_split_over_heavy_expert(T, k):
+    """One expert receives more rows than one weight-gradient chunk (2048): its dW is summed
+    from fp32 chunk partials in chunk order (two and three chunks here)."""
+    E = 4
+    bias = np.zeros(E, np.float32)
+    bias[1] = 10.0
+    inp = _inputs(T, 128, 128, E, k, 27, bias)
+    print(f"[case] split-K heavy expert T={T} k={k}", flush=True)
+    gl = GpuLayer(inp).run()
+    ref = oracle_full(inp)
+    assert ref["plan"].counts[1] > 2048
+    check_full_parity(gl, ref)
