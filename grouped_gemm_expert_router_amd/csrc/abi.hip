@@ -25,22 +25,31 @@ int check_dims(const moe_dims* d) {
   if (d->d <= 0 || d->f <= 0 || d->d % 128 || d->f % 128 || d->d > 65536 || d->f > 65536) return MOE_ERR_SHAPE;
   if (d->T * d->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if (d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3) return MOE_ERR_DTYPE;
+  // the fp8 tiles are 256 columns wide along both d and f
+  if (d->dtype == MOE_FP8_E4M3 && (d->d % 256 || d->f % 256)) return MOE_ERR_SHAPE;
   // launch grids of the ragged GEMMs must fit in 32 bits
   const int64_t A = d->T * d->k;
-  const int64_t rows = (A + kGemmBM - 1) / kGemmBM + (A < d->E ? A : d->E);
+  const int bm = d->dtype == MOE_FP8_E4M3 ? kFp8BM : kGemmBM;
+  const int64_t rows = (A + bm - 1) / bm + (A < d->E ? A : d->E);
   if (rows * (d->f / 64 > d->d / 128 ? d->f / 64 : d->d / 128) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
+
+bool is_fp8(const moe_dims* d) { return d->dtype == MOE_FP8_E4M3; }
+int row_tile(const moe_dims* d) { return is_fp8(d) ? kFp8BM : kGemmBM; }
+// d_topk_w partial sums per routed pair written by the activation-gradient GEMM
+int dact_parts(const moe_dims* d) { return is_fp8(d) ? (int)d->f / 256 : (int)d->f / dact_bn((int)d->f); }
 
 MoeShape shape_of(const moe_dims* d) {
   return MoeShape{(int)d->T, (int)d->d, (int)d->f, (int)d->E, (int)d->k};
 }
 
+// fp8 only: asq/ass (As in e4m3 + scales); dyq/dys, dHq/dHs, xb (x dequantised to bf16).
 struct FwdLayout {
-  size_t tiles, ntiles, op, total;
+  size_t tiles, ntiles, op, asq, ass, total;
 };
 struct BwdLayout {
-  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, total;
+  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dHq, dHs, xb, total;
   int max_partials;
 };
 struct SavedLayout {
@@ -52,11 +61,17 @@ FwdLayout fwd_layout(const moe_dims* d) {
   FwdLayout L{};
   size_t off = 0;
   L.tiles = off;
-  off += al256((size_t)max_row_tiles(A, (int)d->E, kGemmBM) * sizeof(int2) + 16);
+  off += al256((size_t)max_row_tiles(A, (int)d->E, row_tile(d)) * sizeof(int2) + 16);
   L.ntiles = off;
   off += 256;
   L.op = off;
   off += al256((size_t)A * d->d * 2);
+  if (is_fp8(d)) {
+    L.asq = off;
+    off += al256((size_t)A * d->f);
+    L.ass = off;
+    off += al256((size_t)A * (d->f / 128) * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -66,7 +81,7 @@ BwdLayout bwd_layout(const moe_dims* d) {
   BwdLayout L{};
   size_t off = 0;
   L.tiles = off;
-  off += al256((size_t)max_row_tiles(A, (int)d->E, kGemmBM) * sizeof(int2) + 16);
+  off += al256((size_t)max_row_tiles(A, (int)d->E, row_tile(d)) * sizeof(int2) + 16);
   L.ntiles = off;
   off += 256;
   L.tokrow = off;
@@ -76,7 +91,7 @@ BwdLayout bwd_layout(const moe_dims* d) {
   L.dXp = off;
   off += al256((size_t)A * d->d * 2);
   L.dwp = off;
-  off += al256((size_t)A * (d->f / dact_bn((int)d->f)) * sizeof(float));
+  off += al256((size_t)A * dact_parts(d) * sizeof(float));
   L.max_partials = wg_max_partials(shape_of(d));
   L.wg_units = off;
   off += al256((size_t)(d->E + L.max_partials) * sizeof(int2));
@@ -86,6 +101,18 @@ BwdLayout bwd_layout(const moe_dims* d) {
   off += al256((size_t)d->E * sizeof(int32_t));
   L.wg_partial = off;
   off += al256((size_t)L.max_partials * d->d * 2 * d->f * sizeof(float));
+  if (is_fp8(d)) {
+    L.dyq = off;
+    off += al256((size_t)d->T * d->d);
+    L.dys = off;
+    off += al256((size_t)d->T * (d->d / 128) * sizeof(float));
+    L.dHq = off;
+    off += al256((size_t)A * 2 * d->f);
+    L.dHs = off;
+    off += al256((size_t)A * (2 * d->f / 128) * sizeof(float));
+    L.xb = off;
+    off += al256((size_t)d->T * d->d * 2);
+  }
   L.total = off;
   return L;
 }
@@ -195,13 +222,15 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
                 void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
-  if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
-  if (x_scale || W1_scale || W2_scale) return MOE_ERR_DTYPE;
+  const bool fp8 = is_fp8(dims);
+  if (!fp8 && (x_scale || W1_scale || W2_scale)) return MOE_ERR_DTYPE;
   if (dims->T == 0) return MOE_OK;  // an empty layer has nothing to compute
   if (!x || !W1 || !W2 || !topk_w || !offsets || !perm || !inv_perm || !y || !saved || !ws) return MOE_ERR_NULL;
+  if (fp8 && (!x_scale || !W1_scale || !W2_scale)) return MOE_ERR_NULL;
   const FwdLayout L = fwd_layout(dims);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!al16(x) || !al16(W1) || !al16(W2) || !al16(y) || !al256p(saved) || !al256p(ws)) return MOE_ERR_ALIGN;
+  if (fp8 && (!al16(x_scale) || !al16(W1_scale) || !al16(W2_scale))) return MOE_ERR_ALIGN;
   const MoeShape s = shape_of(dims);
   const SavedLayout SL = saved_layout(dims);
   char* w = (char*)ws;
@@ -212,6 +241,17 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
   uint16_t* H = (uint16_t*)(sv + SL.H);
   uint16_t* As = (uint16_t*)(sv + SL.As);
   hipStream_t st = (hipStream_t)stream;
+  if (fp8) {
+    uint8_t* Asq = (uint8_t*)(w + L.asq);
+    float* Ass = (float*)(w + L.ass);
+    const uint8_t *x8 = (const uint8_t*)x, *W18 = (const uint8_t*)W1, *W28 = (const uint8_t*)W2;
+    MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
+    MOE_TRY("gemm_up", launch_fp8_up(s, x8, x_scale, W18, W1_scale, topk_w, offsets, perm, tiles, ntiles, H, As, Asq,
+                                     Ass, st));
+    MOE_TRY("gemm_down", launch_fp8_down(s, Asq, Ass, W28, W2_scale, offsets, perm, tiles, ntiles, Op, st));
+    MOE_TRY("combine", launch_combine(Op, inv_perm, s.T, s.d, s.k, (uint16_t*)y, st));
+    return MOE_OK;
+  }
   MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kGemmBM, tiles, ntiles, st));
   MOE_TRY("gemm_up", launch_gemm_up(s, (const uint16_t*)x, (const uint16_t*)W1, topk_w, offsets, perm, tiles, ntiles, H, As, st));
   MOE_TRY("gemm_down", launch_gemm_down(s, As, (const uint16_t*)W2, offsets, perm, tiles, ntiles, Op, st));
@@ -227,8 +267,8 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                  size_t ws_bytes, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
-  if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
-  if (x_scale || W1_scale || W2_scale) return MOE_ERR_DTYPE;
+  const bool fp8 = is_fp8(dims);
+  if (!fp8 && (x_scale || W1_scale || W2_scale)) return MOE_ERR_DTYPE;
   if (dims->T == 0) {
     // no routed pair: every expert's weight gradient is exactly zero, nothing else to write
     if (!offsets || !dW1 || !dW2 || !ws) return MOE_ERR_NULL;
@@ -247,11 +287,13 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
       !d_topk_w || !ws)
     return MOE_ERR_NULL;
   if (d_logits && !topk_ids) return MOE_ERR_NULL;
+  if (fp8 && (!x_scale || !W1_scale || !W2_scale)) return MOE_ERR_NULL;
   const BwdLayout L = bwd_layout(dims);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!al16(dy) || !al16(x) || !al16(W1) || !al16(W2) || !al16(dx) || !al16(dW1) || !al16(dW2) || !al256p(saved) ||
       !al256p(ws))
     return MOE_ERR_ALIGN;
+  if (fp8 && (!al16(x_scale) || !al16(W1_scale) || !al16(W2_scale))) return MOE_ERR_ALIGN;
   const MoeShape s = shape_of(dims);
   const SavedLayout SL = saved_layout(dims);
   char* w = (char*)ws;
@@ -265,19 +307,43 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   const uint16_t* H = (const uint16_t*)(sv + SL.H);
   const uint16_t* As = (const uint16_t*)(sv + SL.As);
   hipStream_t st = (hipStream_t)stream;
+  const WgSplit sp = wg_split_of(L, w, offsets);
+  if (fp8) {
+    uint8_t* dyq = (uint8_t*)(w + L.dyq);
+    float* dys = (float*)(w + L.dys);
+    uint8_t* dHq = (uint8_t*)(w + L.dHq);
+    float* dHs = (float*)(w + L.dHs);
+    uint16_t* xb = (uint16_t*)(w + L.xb);
+    const uint8_t *W18 = (const uint8_t*)W1, *W28 = (const uint8_t*)W2;
+    MOE_TRY("quant_dy", launch_quant_rows((const uint16_t*)dy, s.T, s.d, dyq, dys, st));
+    MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
+    MOE_TRY("gemm_dact", launch_fp8_dact(s, dyq, dys, W28, W2_scale, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq,
+                                         dHs, dwp, st));
+    MOE_TRY("gemm_dx", launch_fp8_dx(s, dHq, dHs, W18, W1_scale, offsets, perm, tiles, ntiles, dXp, st));
+    MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
+    MOE_TRY("dequant_x", launch_dequant_rows((const uint8_t*)x, x_scale, s.T, s.d, xb, st));
+    MOE_TRY("tokrow", launch_tokrow(perm, offsets, s.E, (int64_t)s.T * s.k, s.k, tokrow, st));
+    MOE_TRY("wg_split", launch_wg_split(s, offsets, sp, st));
+    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, sp, (uint16_t*)dW2, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.f * s.d, (uint16_t*)dW2, st));
+    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, xb, dH, offsets, perm, tokrow, sp, (uint16_t*)dW1, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.d * 2 * s.f, (uint16_t*)dW1, st));
+    MOE_TRY("dlogits", launch_dlogits(dwp, dact_parts(dims), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w,
+                                      d_logits, st));
+    return MOE_OK;
+  }
   MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kGemmBM, tiles, ntiles, st));
   MOE_TRY("gemm_dact", launch_gemm_dact(s, (const uint16_t*)dy, (const uint16_t*)W2, H, topk_w, offsets, perm, tiles, ntiles, dH,
                            dwp, st));
   MOE_TRY("gemm_dx", launch_gemm_dx(s, dH, (const uint16_t*)W1, offsets, perm, tiles, ntiles, dXp, st));
   MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
-  const WgSplit sp = wg_split_of(L, w, offsets);
   MOE_TRY("tokrow", launch_tokrow(perm, offsets, s.E, (int64_t)s.T * s.k, s.k, tokrow, st));
   MOE_TRY("wg_split", launch_wg_split(s, offsets, sp, st));
   MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, sp, (uint16_t*)dW2, st));
   MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.f * s.d, (uint16_t*)dW2, st));
   MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, tokrow, sp, (uint16_t*)dW1, st));
   MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.d * 2 * s.f, (uint16_t*)dW1, st));
-  MOE_TRY("dlogits", launch_dlogits(dwp, s.f / dact_bn(s.f), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
+  MOE_TRY("dlogits", launch_dlogits(dwp, dact_parts(dims), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
                                    st));
 
   return MOE_OK;

@@ -1,0 +1,107 @@
+// Device building blocks shared by the bf16 and fp8 grouped GEMMs (gfx950): LDS DMA with
+// explicit wait counts, XCD-aware block numbering, swizzled LDS operand layouts and the MFMA
+// operand reads (ds_read_b128 for K-contiguous tiles, LDS transpose reads for N-contiguous ones).
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  Renumber them so
+// XCD j runs a contiguous range of logical tiles: neighbouring tiles share an expert's weights
+// and a block of token rows, and now share one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  constexpr int NX = 8;
+  const int q = G / NX, r = G % NX;
+  const int x = bid % NX, i = bid / NX;
+  return x * q + min(x, r) + i;
+}
+
+// ---------------------------------------------------------------- LDS DMA and barriers
+// global_load_lds_dwordx4 copies each lane's 16 bytes to LDS at m0 + 16*lane.  It is issued
+// through inline asm so the compiler's wait-count pass does not make every LDS read wait for
+// all DMA in flight; the kernel waits explicitly (vm_wait_barrier) before the barrier that
+// publishes a stage.  One wait state separates the m0 write from the DMA.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_byte_addr)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// Same, also waiting for this wave's LDS reads (and scalar loads) before the barrier, so a
+// stage another wave refills right after it can have no read of this wave still pending.
+template <int N>
+__device__ __forceinline__ void vm_lgkm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+// Operand tiles in LDS (16-byte chunks, XOR-swizzled so the 16 lanes an LDS cycle serves hit
+// 16 distinct 16-byte bank groups of the 64-bank LDS):
+//   KM: [row][BK] for K-contiguous sources.  BK = 32: row = 64 bytes = 4 chunks, chunk c of
+//       row r lives at chunk c ^ ((r >> 2) & 3); BK = 64: row = 128 bytes = 8 chunks, chunk c
+//       at c ^ ((r >> 1) & 7).  MFMA operand = one ds_read_b128.
+//   KN: [k][C] for sources contiguous along M or N; k row = 2C bytes; chunk c of k row r lives
+//       at chunk c ^ (4 * (r & 3)).  MFMA operand = two ds_read_b64_tr_b16: within a 16-lane
+//       group, lane s supplies the address of (k = k0 + s/4, col = c0 + 4*(s%4)) and lane i
+//       receives the 4 values (k0..k0+3, c0 + i).
+template <int BK>
+__device__ __forceinline__ uint32_t km_off(int row, int c) {
+  if constexpr (BK == 32) return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
+  else return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+}
+template <int C>
+__device__ __forceinline__ uint32_t kn_off(int kr, int col) {
+  return kr * (2 * C) + ((((col >> 3) ^ (4 * (kr & 3)))) << 4) + ((col & 7) << 1);
+}
+
+template <int BK>
+__device__ __forceinline__ bf16x8_t read_km(uint32_t base, int row, int c) {
+  return *(const LDS_AS bf16x8_t*)(uintptr_t)(base + km_off<BK>(row, c));
+}
+// 32-column fragment at column cbase, k16 step kk: lane holds column cbase + lane%32 and
+// k = 16*kk + 8*(lane/32) + 0..7.
+template <int C>
+__device__ __forceinline__ bf16x8_t read_kn(uint32_t base, int cbase, int kk, int lane) {
+  const int grp = lane >> 4, i16 = lane & 15;
+  const int col = cbase + 16 * (grp & 1) + 4 * (i16 & 3);
+  const int kr0 = 16 * kk + 8 * (grp >> 1) + (i16 >> 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)(base + kn_off<C>(kr0, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(uintptr_t)(base + kn_off<C>(kr0 + 4, col)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// LDS DMA of one dword per lane (to m0 + 4*lane).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(lds_byte_addr)
+               : "memory", "m0");
+}
+
+}  // namespace moe

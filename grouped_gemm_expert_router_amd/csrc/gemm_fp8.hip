@@ -1,0 +1,588 @@
+// Ragged grouped GEMMs on gfx950 fp8 MFMA (OCP e4m3, v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// block exponents) with fp32 block scales: activations carry one scale per row per 128 values
+// of K, weights one per 128x128 block.  Blockwise FP8 is one of the data types of the fused MoE
+// backward on the Prime Mega MoE page ("Prime Mega MoE: tanításra is jó a DeepSeek MoE
+// kernele", section "Mit csinált a Prime Intellect?"); quantisation adds work on top of the
+// 16-bit master weights (TE MoE page "NVIDIA מציגה דרך יעילה לאמן מודלי MoE בביולוגיה",
+// section "צמצום הזיכרון ותקורות הכימות").
+//
+// One K stage is exactly one 128-wide scale block: the stage's two 64-deep MFMAs accumulate
+// into a temporary, which is then promoted into the fp32 accumulator with s_a(row) * s_b(block).
+// Tiles are 128 x 256 x 128 with 8 waves (2 x 4), each owning 64 x 64.  Operands reach LDS by
+// DMA; K-contiguous tiles are read with ds_read_b128, N-contiguous weight tiles with the 8-bit
+// LDS transpose read.  The row scales of each stage arrive by DMA as well.
+//
+// Epilogues: UP writes H (bf16, kept for the backward), As = w * silu(g) * u in bf16 (for the
+// weight gradient) and requantised to e4m3 with one scale per row per 128 columns (the next
+// GEMM's K); DACT writes dH in bf16 and requantised the same way, plus the routing-weight
+// partials; DOWN and DX write bf16 rows in slot order.
+#include "common.hpp"
+#include "gemm_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+enum Fp8Mode { F_UP = 0, F_DOWN = 1, F_DACT = 2, F_DX = 3 };
+
+struct Fp8Args {
+  const uint8_t* A;        // fp8 rows, K contiguous
+  int64_t lda;             // bytes
+  const float* A_scale;    // [rows, K/128]
+  int64_t lds_a;           // floats per scale row
+  const uint8_t* B;        // fp8 weights of all experts
+  int64_t ldb, b_estride;  // bytes
+  const float* B_scale;    // per expert [rows/128, cols/128] of B as stored
+  int64_t bs_estride;
+  int bs_ld;
+  int N, K, kslots, f;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int2* tiles;
+  const int32_t* ntiles;
+  int gatherA;
+  const float* topk_w;
+  uint16_t* C0;
+  int64_t ldc0;
+  uint16_t* C1;
+  int64_t ldc1;
+  uint8_t* Q;  // requantised output (UP: As, DACT: dH)
+  int64_t ldq;
+  float* QS;
+  int64_t ldqs;
+  const uint16_t* Hs;
+  int64_t ldh;
+  float* dwp;
+  int nparts;
+};
+
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// KN fp8 layout: [k][256 bytes]; chunk c (16 columns) of k row r lives at chunk c ^ (2 * (r & 7)).
+__device__ __forceinline__ uint32_t kn8_off(int kr, int col) {
+  return kr * 256 + ((((col >> 4) ^ (2 * (kr & 7)))) << 4) + (col & 15);
+}
+
+// 32-column fragment at column cbase, 64-deep step kk: lane holds column cbase + lane%32 and
+// k = 64*kk + 32*(lane/32) + 0..31.  Within a 16-lane group, lane s supplies the address of
+// (k = k0 + s/2, col = c0 + 8*(s%2)) and lane i receives the 8 bytes (k0..k0+7, c0 + i).
+__device__ __forceinline__ i32x8 read_kn8(uint32_t base, int cbase, int kk, int lane) {
+  const int grp = lane >> 4, i16 = lane & 15;
+  const int col = cbase + 16 * (grp & 1) + 8 * (i16 & 1);
+  const int krb = 64 * kk + 32 * (grp >> 1) + (i16 >> 1);
+  i32x8 v;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const i32x2v t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2v*)(uintptr_t)(base + kn8_off(krb + 8 * h, col)));
+    v[2 * h] = t.x;
+    v[2 * h + 1] = t.y;
+  }
+  return v;
+}
+
+// KM fp8 layout: [row][128 bytes], chunk c of row r at chunk c ^ ((r >> 1) & 7); 32 bytes per
+// lane = two chunks.
+__device__ __forceinline__ i32x8 read_km8(uint32_t base, int row, int kk, int lane) {
+  const int c = 4 * kk + 2 * (lane >> 5);
+  const u32x4 lo = *(const LDS_AS u32x4*)(uintptr_t)(base + km_off<64>(row, c));
+  const u32x4 hi = *(const LDS_AS u32x4*)(uintptr_t)(base + km_off<64>(row, c + 1));
+  i32x8 v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// e4m3 with round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  auto sat = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
+}
+
+// Quantise 8 values of a 128-wide block held by 16 consecutive lanes: scale = amax / 448 of the
+// block (1 when all are zero); returns the 8 codes and sets *scale.
+__device__ __forceinline__ u32x2 quant8_group16(const float (&v)[8], float* scale) {
+  float m = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
+#pragma unroll
+  for (int s = 8; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+  const float sc = m > 0.0f ? m / 448.0f : 1.0f;
+  const float inv = m > 0.0f ? 448.0f / m : 1.0f;
+  *scale = sc;
+  u32x2 q;
+  q.x = pack_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  q.y = pack_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  return q;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args g) {
+  constexpr int BM = 128, BN = 256, BK = 128, S = 2, WM = 2, WN = 4, NW = 8, NTH = 512;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr bool B_KN = (MODE == F_UP || MODE == F_DOWN);
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, SC_BYTES = NW * 256;
+  constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
+  constexpr int QA = A_BYTES / (1024 * NW), QB = B_BYTES / (1024 * NW);
+  constexpr int CPAD = BN + 4;
+  constexpr int CBAND_BYTES = 2 * 32 * CPAD * 4;
+  constexpr int ARENA = S * STAGE > CBAND_BYTES ? S * STAGE : CBAND_BYTES;
+  static_assert(QA == 2 && QB == 4, "DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ARENA];
+  float* cband = reinterpret_cast<float*>(smem);
+  __shared__ float s_w[BM];
+  __shared__ int s_slot[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
+
+  // ------------------------------------------------------------------ tile coordinates
+  const int nN = (MODE == F_UP) ? g.f / (BN / 2) : g.N / BN;
+  const int G_valid = *(const CONST_AS int32_t*)g.ntiles * nN;
+  if ((int)blockIdx.x >= G_valid) return;
+  const int lid = xcd_remap(blockIdx.x, G_valid);
+  const int nt = lid % nN;
+  const int2 te = g.tiles[lid / nN];
+  const int e = te.x;
+  const int m0 = g.offsets[e] + te.y * BM;
+  const int mrows = min(BM, g.offsets[e + 1] - m0);
+  const int n0 = (MODE == F_UP) ? nt * (BN / 2) : nt * BN;
+  for (int r = tid; r < BM; r += NTH) {
+    int p = -1;
+    float wv = 0.0f;
+    if (r < mrows) {
+      p = g.perm[m0 + r];
+      if (MODE == F_UP || MODE == F_DACT) wv = g.topk_w[p];
+    }
+    s_slot[r] = p;
+    s_w[r] = wv;
+  }
+  const uint8_t* Bexp = g.B + (int64_t)e * g.b_estride;
+  const CONST_AS float* Bs = (const CONST_AS float*)g.B_scale + (int64_t)e * g.bs_estride;
+
+  // ------------------------------------------------------------------ DMA sources
+  // A (KM, 128 rows x 128 bytes): block gi = 2*wave + q holds rows 8*gi..8*gi+7.
+  const uint8_t* a_src[QA];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int row = 8 * (wave * QA + q) + lane / 8;
+    const int c = (lane % 8) ^ ((row >> 1) & 7);
+    const int pos = m0 + (row < mrows ? row : 0);  // rows past the expert feed unstored outputs
+    const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
+    a_src[q] = g.A + src * g.lda + 16 * c;
+  }
+  // A row scales: wave w brings rows 16w..16w+15 (lanes past 15 repeat row 16w + 15).
+  const float* sc_src;
+  {
+    const int row = 16 * wave + min(lane, 15);
+    const int pos = m0 + (row < mrows ? row : 0);
+    const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
+    sc_src = g.A_scale + src * g.lds_a;
+  }
+  const uint8_t* b_src[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    if constexpr (B_KN) {
+      // k rows 4*gi + lane/16 (256 bytes each), chunk lane%16 holds logical chunk c
+      const int kr = 4 * (wave * QB + q) + lane / 16;
+      const int c = (lane % 16) ^ (2 * (kr & 7));
+      int col;
+      if constexpr (MODE == F_UP) col = c < 8 ? n0 + 16 * c : g.f + n0 + 16 * (c - 8);
+      else col = n0 + 16 * c;
+      b_src[q] = Bexp + (int64_t)kr * g.ldb + col;
+    } else {
+      const int row = 8 * (wave * QB + q) + lane / 8;
+      const int c = (lane % 8) ^ ((row >> 1) & 7);
+      b_src[q] = Bexp + (int64_t)(n0 + row) * g.ldb + 16 * c;
+    }
+  }
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    const int k0 = t * BK;
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, sbase = bbase + B_BYTES;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) dma16(a_src[q] + k0, abase + (wave * QA + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+      dma16(B_KN ? b_src[q] + (int64_t)k0 * g.ldb : b_src[q] + k0, bbase + (wave * QB + q) * 1024);
+    dma4(sc_src + t, sbase + wave * 256);
+  };
+
+  // LDS column of the wave's j-th 32-column B fragment (UP: gate fragments, then up fragments)
+  auto b_row = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (MODE == F_UP)
+      return j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32;
+    else
+      return wn * TN + j * 32;
+  };
+  // 128-column block of the weight matrix holding B fragment j
+  auto b_block = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (MODE == F_UP)
+      return j < FN / 2 ? nt : g.f / 128 + nt;  // BN/2 = 128: the gate (up) columns of a tile are one block
+    else
+      return (n0 + wn * TN + j * 32) / 128;
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto compute = [&](int st, int kb) __attribute__((always_inline)) {
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, sbase = bbase + B_BYTES;
+    f32x16_t t[FM][FN];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      i32x8 af[FM], bv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = read_km8(abase, wm * TM + i * 32 + (lane & 31), kk, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (B_KN) bv[j] = read_kn8(bbase, b_row(j), kk, lane);
+        else bv[j] = read_km8(bbase, b_row(j) + (lane & 31), kk, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const f32x16_t z = {};
+          t[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bv[j], kk == 0 ? z : t[i][j], 0, 0, 0,
+                                                                     127, 0, 127);
+        }
+    }
+    // promote: acc += t * s_a(row) * s_b(block of the fragment's columns)
+    float sb[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nb = b_block(j);
+      sb[j] = B_KN ? Bs[(int64_t)kb * g.bs_ld + nb] : Bs[(int64_t)nb * g.bs_ld + kb];
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float sa[16];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = wm * TM + i * 32 + 8 * rr + 4 * (lane >> 5);  // 4 consecutive rows
+        const f32x4_t v = *(const LDS_AS f32x4_t*)(uintptr_t)(sbase + (row >> 4) * 256 + (row & 15) * 4);
+        sa[4 * rr] = v[0];
+        sa[4 * rr + 1] = v[1];
+        sa[4 * rr + 2] = v[2];
+        sa[4 * rr + 3] = v[3];
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[i][j][r], sa[r] * sb[j], acc[i][j][r]);
+    }
+  };
+
+  // ------------------------------------------------------------------ main loop (2 stages)
+  const int nk = g.K / BK;
+  __syncthreads();
+  issue(0, 0);
+  for (int it = 0; it < nk; ++it) {
+    vm_lgkm_wait_barrier<0>();
+    if (it + 1 < nk) issue(it + 1, (it + 1) % S);
+    compute(it % S, it);
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------------ epilogues (LDS band)
+  const int lcol = lane & 31;
+  constexpr int CH = BN / 8;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = b_row(j) + lcol;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        cband[q * CPAD + c] = acc[i][j][r];
+      }
+    }
+    __syncthreads();
+    auto tile_row = [&](int q) __attribute__((always_inline)) { return (q >> 5) * TM + 32 * i + (q & 31); };
+    if constexpr (MODE == F_UP) {
+      // 16 lanes per row: 8 gate + 8 up columns each; As's 128 columns of the tile form one block
+      for (int id = tid; id < 64 * (CH / 2); id += NTH) {
+        const int q = id / (CH / 2), cc = id % (CH / 2);
+        const int lr = tile_row(q);
+        const bool ok = lr < mrows;
+        const float* gp = &cband[q * CPAD + cc * 8];
+        const float* up = &cband[q * CPAD + BN / 2 + cc * 8];
+        const float w = s_w[lr];
+        float as[8];
+        uint32_t hg[4], hu[4], ab[4];
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+          const float g0 = gp[2 * t2], g1 = gp[2 * t2 + 1], u0 = up[2 * t2], u1 = up[2 * t2 + 1];
+          hg[t2] = pack_bf16x2(g0, g1);
+          hu[t2] = pack_bf16x2(u0, u1);
+          as[2 * t2] = w * g0 * sigmoidf_fast(g0) * u0;
+          as[2 * t2 + 1] = w * g1 * sigmoidf_fast(g1) * u1;
+          ab[t2] = pack_bf16x2(as[2 * t2], as[2 * t2 + 1]);
+        }
+        float sc;
+        const u32x2 qv = quant8_group16(as, &sc);
+        if (ok) {
+          const int64_t pos = m0 + lr;
+          const int col = n0 + cc * 8;
+          *(uint4*)&g.C0[pos * g.ldc0 + col] = make_uint4(hg[0], hg[1], hg[2], hg[3]);
+          *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(hu[0], hu[1], hu[2], hu[3]);
+          *(uint4*)&g.C1[pos * g.ldc1 + col] = make_uint4(ab[0], ab[1], ab[2], ab[3]);
+          *(u32x2*)&g.Q[pos * g.ldq + col] = qv;
+          if (cc == 0) g.QS[pos * g.ldqs + nt] = sc;
+        }
+      }
+    } else if constexpr (MODE == F_DACT) {
+      // 32 lanes per row (8 columns each): dSwiGLU, routing-weight partial, dH in bf16 and e4m3
+      for (int id = tid; id < 64 * CH; id += NTH) {
+        const int q = id / CH, cc = id % CH;
+        const int lr = tile_row(q);
+        const bool ok = lr < mrows;
+        const int64_t pos = m0 + (ok ? lr : 0);
+        const int col = n0 + cc * 8;
+        const uint4 hgv = *(const uint4*)&g.Hs[pos * g.ldh + col];
+        const uint4 huv = *(const uint4*)&g.Hs[pos * g.ldh + g.f + col];
+        const float* Gp = &cband[q * CPAD + cc * 8];
+        const float w = s_w[lr];
+        float part = 0.0f, dg[8], du[8];
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+          const uint32_t wg = word_of(hgv, t2), wu = word_of(huv, t2);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float gv = hh ? hi_bf16(wg) : lo_bf16(wg), uv = hh ? hi_bf16(wu) : lo_bf16(wu);
+            const float G = Gp[2 * t2 + hh];
+            const float sg = sigmoidf_fast(gv), sl = gv * sg, da = w * G;
+            part += G * (sl * uv);
+            dg[2 * t2 + hh] = da * uv * sg * (1.0f + gv * (1.0f - sg));
+            du[2 * t2 + hh] = da * sl;
+          }
+        }
+        float sg_, su_;
+        const u32x2 qg = quant8_group16(dg, &sg_);
+        const u32x2 qu = quant8_group16(du, &su_);
+#pragma unroll
+        for (int m = CH / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+        if (ok) {
+          *(uint4*)&g.C0[pos * g.ldc0 + col] = make_uint4(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
+                                                          pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7]));
+          *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
+                                                                pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7]));
+          *(u32x2*)&g.Q[pos * g.ldq + col] = qg;
+          *(u32x2*)&g.Q[pos * g.ldq + g.f + col] = qu;
+          if ((cc & 15) == 0) {
+            g.QS[pos * g.ldqs + col / 128] = sg_;
+            g.QS[pos * g.ldqs + (g.f + col) / 128] = su_;
+          }
+          if (cc == 0) g.dwp[pos * g.nparts + nt] = part;
+        }
+      }
+    } else {
+      for (int id = tid; id < 64 * CH; id += NTH) {
+        const int q = id / CH, cc = id % CH;
+        const int lr = tile_row(q);
+        if (lr < mrows) {
+          const float* cp = &cband[q * CPAD + cc * 8];
+          const uint4 o = make_uint4(pack_bf16x2(cp[0], cp[1]), pack_bf16x2(cp[2], cp[3]),
+                                     pack_bf16x2(cp[4], cp[5]), pack_bf16x2(cp[6], cp[7]));
+          *(uint4*)&g.C0[(int64_t)s_slot[lr] * g.ldc0 + n0 + cc * 8] = o;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------- host launchers
+namespace {
+template <int MODE>
+hipError_t run_fp8(const Fp8Args& g, int64_t A, int E, int nN, hipStream_t st) {
+  const int64_t blocks = (int64_t)max_row_tiles(A, E, kFp8BM) * nN;
+  if (blocks == 0) return hipSuccess;
+  grouped_gemm_fp8_kernel<MODE><<<(unsigned)blocks, 512, 0, st>>>(g);
+  return hipGetLastError();
+}
+Fp8Args fp8_base(const MoeShape& s, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                 const int32_t* ntiles) {
+  Fp8Args g{};
+  g.kslots = s.k;
+  g.f = s.f;
+  g.offsets = offsets;
+  g.perm = perm;
+  g.tiles = tiles;
+  g.ntiles = ntiles;
+  return g;
+}
+}  // namespace
+
+hipError_t launch_fp8_up(const MoeShape& s, const uint8_t* x, const float* xs, const uint8_t* W1, const float* W1s,
+                         const float* topk_w, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                         const int32_t* ntiles, uint16_t* H, uint16_t* As, uint8_t* Asq, float* Ass, hipStream_t st) {
+  Fp8Args g = fp8_base(s, offsets, perm, tiles, ntiles);
+  g.A = x;
+  g.lda = s.d;
+  g.A_scale = xs;
+  g.lds_a = s.d / 128;
+  g.gatherA = 1;
+  g.B = W1;
+  g.ldb = 2 * (int64_t)s.f;
+  g.b_estride = (int64_t)s.d * 2 * s.f;
+  g.B_scale = W1s;
+  g.bs_estride = (int64_t)(s.d / 128) * (2 * s.f / 128);
+  g.bs_ld = 2 * s.f / 128;
+  g.N = 2 * s.f;
+  g.K = s.d;
+  g.topk_w = topk_w;
+  g.C0 = H;
+  g.ldc0 = 2 * (int64_t)s.f;
+  g.C1 = As;
+  g.ldc1 = s.f;
+  g.Q = Asq;
+  g.ldq = s.f;
+  g.QS = Ass;
+  g.ldqs = s.f / 128;
+  return run_fp8<F_UP>(g, (int64_t)s.T * s.k, s.E, s.f / 128, st);
+}
+
+hipError_t launch_fp8_down(const MoeShape& s, const uint8_t* Asq, const float* Ass, const uint8_t* W2,
+                           const float* W2s, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                           const int32_t* ntiles, uint16_t* Op, hipStream_t st) {
+  Fp8Args g = fp8_base(s, offsets, perm, tiles, ntiles);
+  g.A = Asq;
+  g.lda = s.f;
+  g.A_scale = Ass;
+  g.lds_a = s.f / 128;
+  g.B = W2;
+  g.ldb = s.d;
+  g.b_estride = (int64_t)s.f * s.d;
+  g.B_scale = W2s;
+  g.bs_estride = (int64_t)(s.f / 128) * (s.d / 128);
+  g.bs_ld = s.d / 128;
+  g.N = s.d;
+  g.K = s.f;
+  g.C0 = Op;
+  g.ldc0 = s.d;
+  return run_fp8<F_DOWN>(g, (int64_t)s.T * s.k, s.E, s.d / 256, st);
+}
+
+hipError_t launch_fp8_dact(const MoeShape& s, const uint8_t* dyq, const float* dys, const uint8_t* W2,
+                           const float* W2s, const uint16_t* H, const float* topk_w, const int32_t* offsets,
+                           const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* dH, uint8_t* dHq,
+                           float* dHs, float* dwp, hipStream_t st) {
+  Fp8Args g = fp8_base(s, offsets, perm, tiles, ntiles);
+  g.A = dyq;
+  g.lda = s.d;
+  g.A_scale = dys;
+  g.lds_a = s.d / 128;
+  g.gatherA = 1;
+  g.B = W2;  // row n of W2[e] ([f, d]) is column n of W2[e]^T, contiguous in K = d
+  g.ldb = s.d;
+  g.b_estride = (int64_t)s.f * s.d;
+  g.B_scale = W2s;
+  g.bs_estride = (int64_t)(s.f / 128) * (s.d / 128);
+  g.bs_ld = s.d / 128;
+  g.N = s.f;
+  g.K = s.d;
+  g.topk_w = topk_w;
+  g.Hs = H;
+  g.ldh = 2 * (int64_t)s.f;
+  g.C0 = dH;
+  g.ldc0 = 2 * (int64_t)s.f;
+  g.Q = dHq;
+  g.ldq = 2 * (int64_t)s.f;
+  g.QS = dHs;
+  g.ldqs = 2 * s.f / 128;
+  g.dwp = dwp;
+  g.nparts = s.f / 256;
+  return run_fp8<F_DACT>(g, (int64_t)s.T * s.k, s.E, s.f / 256, st);
+}
+
+hipError_t launch_fp8_dx(const MoeShape& s, const uint8_t* dHq, const float* dHs, const uint8_t* W1, const float* W1s,
+                         const int32_t* offsets, const int32_t* perm, const int2* tiles, const int32_t* ntiles,
+                         uint16_t* dXp, hipStream_t st) {
+  Fp8Args g = fp8_base(s, offsets, perm, tiles, ntiles);
+  g.A = dHq;
+  g.lda = 2 * (int64_t)s.f;
+  g.A_scale = dHs;
+  g.lds_a = 2 * s.f / 128;
+  g.B = W1;  // row n of W1[e] ([d, 2f]) is column n of W1[e]^T, contiguous in K = 2f
+  g.ldb = 2 * (int64_t)s.f;
+  g.b_estride = (int64_t)s.d * 2 * s.f;
+  g.B_scale = W1s;
+  g.bs_estride = (int64_t)(s.d / 128) * (2 * s.f / 128);
+  g.bs_ld = 2 * s.f / 128;
+  g.N = s.d;
+  g.K = 2 * s.f;
+  g.C0 = dXp;
+  g.ldc0 = s.d;
+  return run_fp8<F_DX>(g, (int64_t)s.T * s.k, s.E, s.d / 256, st);
+}
+
+// ------------------------------------------------------------------ fp8 data movement
+// dy (bf16) -> e4m3 with one scale per row per 128 values; 16 threads per block of 128.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ src, int64_t n8, int cols,
+                                                         uint8_t* __restrict__ q, float* __restrict__ qs) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-value group per thread
+  const bool ok = i < n8;
+  const int64_t ii = ok ? i : 0;
+  const uint4 v = *(const uint4*)(src + ii * 8);
+  float f[8] = {lo_bf16(v.x), hi_bf16(v.x), lo_bf16(v.y), hi_bf16(v.y),
+                lo_bf16(v.z), hi_bf16(v.z), lo_bf16(v.w), hi_bf16(v.w)};
+  float sc;
+  const u32x2 qv = quant8_group16(f, &sc);
+  if (ok) {
+    *(u32x2*)(q + ii * 8) = qv;
+    if ((ii & 15) == 0) {
+      const int64_t row = (ii * 8) / cols, blk = ((ii * 8) % cols) / 128;
+      qs[row * (cols / 128) + blk] = sc;
+    }
+  }
+}
+
+// x (e4m3 with 1x128 scales) -> bf16, for the weight gradient.
+__global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__ qs,
+                                                           int64_t n8, int cols, uint16_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const u32x2 w = *(const u32x2*)(q + i * 8);
+  const int64_t row = (i * 8) / cols, blk = ((i * 8) % cols) / 128;
+  const float s = qs[row * (cols / 128) + blk];
+  float f[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t word = h ? w.y : w.x;
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+    f[4 * h] = a[0] * s;
+    f[4 * h + 1] = a[1] * s;
+    f[4 * h + 2] = b[0] * s;
+    f[4 * h + 3] = b[1] * s;
+  }
+  *(uint4*)(dst + i * 8) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                                      pack_bf16x2(f[6], f[7]));
+}
+
+hipError_t launch_quant_rows(const uint16_t* src, int64_t rows, int cols, uint8_t* q, float* qs, hipStream_t st) {
+  const int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipSuccess;
+  quant_rows_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(src, n8, cols, q, qs);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, int cols, uint16_t* dst,
+                               hipStream_t st) {
+  const int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipSuccess;
+  dequant_rows_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(q, qs, n8, cols, dst);
+  return hipGetLastError();
+}
+
+}  // namespace moe

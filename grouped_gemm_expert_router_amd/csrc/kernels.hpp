@@ -71,6 +71,32 @@ constexpr int kTokrowPad = 64;
 hipError_t launch_tokrow(const int32_t* perm, const int32_t* offsets, int E, int64_t A, int k, int32_t* tokrow,
                          hipStream_t st);
 
+// fp8 (OCP e4m3) grouped GEMMs with fp32 block scales: activations [rows, K/128] (one scale per
+// row per 128 values), weights [E, rows/128, cols/128] of each matrix as stored.  Row tiles are
+// kFp8BM high; d and f must be multiples of 256.
+constexpr int kFp8BM = 128;
+// H = x[perm/k] . W1[e]; As = w * silu(gate) * up in bf16 and as e4m3 + scales [A, f/128].
+hipError_t launch_fp8_up(const MoeShape& s, const uint8_t* x, const float* xs, const uint8_t* W1, const float* W1s,
+                         const float* topk_w, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                         const int32_t* ntiles, uint16_t* H, uint16_t* As, uint8_t* Asq, float* Ass, hipStream_t st);
+// Op[perm[pos]] = As[pos] . W2[e] from the e4m3 As.
+hipError_t launch_fp8_down(const MoeShape& s, const uint8_t* Asq, const float* Ass, const uint8_t* W2,
+                           const float* W2s, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                           const int32_t* ntiles, uint16_t* Op, hipStream_t st);
+// G = dy_q[perm/k] . W2[e]^T; dH in bf16 and e4m3 + scales [A, 2f/128]; f/256 d_topk_w partials.
+hipError_t launch_fp8_dact(const MoeShape& s, const uint8_t* dyq, const float* dys, const uint8_t* W2,
+                           const float* W2s, const uint16_t* H, const float* topk_w, const int32_t* offsets,
+                           const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* dH, uint8_t* dHq,
+                           float* dHs, float* dwp, hipStream_t st);
+// dXp[perm[pos]] = dH_q[pos] . W1[e]^T.
+hipError_t launch_fp8_dx(const MoeShape& s, const uint8_t* dHq, const float* dHs, const uint8_t* W1, const float* W1s,
+                         const int32_t* offsets, const int32_t* perm, const int2* tiles, const int32_t* ntiles,
+                         uint16_t* dXp, hipStream_t st);
+// bf16 rows -> e4m3 + one scale per row per 128 values (cols % 128 == 0), and back to bf16.
+hipError_t launch_quant_rows(const uint16_t* src, int64_t rows, int cols, uint8_t* q, float* qs, hipStream_t st);
+hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, int cols, uint16_t* dst,
+                               hipStream_t st);
+
 // data movement and router backward
 hipError_t launch_permute(const uint16_t* x, const int32_t* perm, const int32_t* offsets, int64_t A, int d, int k,
                           uint16_t* xp, hipStream_t st);

@@ -41,7 +41,10 @@
  *   - Errors: a negative MOE_ERR_* code is returned and nothing is enqueued; MOE_ERR_HIP means
  *     a launch failed (moe_status_string() then names the HIP error).
  *   - Shapes (MOE_ERR_SHAPE otherwise): T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64),
- *     d and f positive multiples of 128 and at most 65536, T*k < 2^31.
+ *     d and f positive multiples of 128 (MOE_FP8_E4M3: of 256) and at most 65536, T*k < 2^31.
+ *   - fp8 (MOE_FP8_E4M3): codes are OCP e4m3 (bias 7, max 448, no infinities); a block's value
+ *     is code * scale with its fp32 scale ([Prime] "Mit csinált a Prime Intellect?": blockwise
+ *     FP8 is one of the kernel's data types).  Outputs and gradients stay bf16/fp32.
  *   - Alignment (MOE_ERR_ALIGN otherwise): tensors 16-byte aligned, ws and saved 256-byte
  *     aligned (every torch/hipMalloc allocation is).
  */
@@ -107,7 +110,11 @@ int moe_plan(const moe_dims* dims, const int32_t* topk_ids, int32_t* counts, int
  * fp32 in slot order with one bf16 rounding.  Each expert is computed at its real row count
  * ([JAX] "Csoportosított mátrixszorzás és összevont adatmozgatás" [grouped GEMM and fused data
  * movement]).  `saved` (moe_saved_bytes) receives what moe_backward needs.  For
- * dtype = MOE_FP8_E4M3 the *_scale arguments are required; for bf16 they must be NULL. */
+ * dtype = MOE_FP8_E4M3 the *_scale arguments are required when T > 0 (MOE_ERR_NULL); for bf16
+ * they must be NULL (MOE_ERR_DTYPE).  fp8: both grouped GEMMs run on e4m3 operands with fp32
+ * accumulation and per-128-K scale promotion; the scaled SwiGLU output feeding the second one
+ * is requantised to e4m3 with one scale (its absolute maximum / 448) per row per 128 columns
+ * ([TE] "צמצום הזיכרון ותקורות הכימות" [reducing memory and quantisation overheads]). */
 int moe_forward(const moe_dims* dims, const void* x, const float* x_scale,
                 const void* W1, const float* W1_scale, const void* W2, const float* W2_scale,
                 const float* topk_w, const int32_t* offsets, const int32_t* perm,
@@ -120,7 +127,10 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale,
  * unrouted slots) and, if d_logits is not NULL, d_logits[t, ids[t,j]] =
  * w[t,j] * (d_topk_w[t,j] - sum_i w[t,i] d_topk_w[t,i]) and 0 elsewhere (the softmax over the
  * kept logits; topk_ids is then required).  `saved` must come from moe_forward on the same
- * inputs.  Every reduction has a fixed order, so results are bitwise reproducible. */
+ * inputs.  Every reduction has a fixed order, so results are bitwise reproducible.
+ * fp8: dy is quantised like the forward activations (1x128 blocks) for the two data-gradient
+ * GEMMs and dH is requantised the same way between them; the weight gradients use bf16
+ * operands (the saved bf16 activations, dy, dH and x dequantised). */
 int moe_backward(const moe_dims* dims, const void* dy, const void* x, const float* x_scale,
                  const void* W1, const float* W1_scale, const void* W2, const float* W2_scale,
                  const int32_t* topk_ids, const float* topk_w, const int32_t* offsets,

@@ -42,10 +42,18 @@ class GpuLayer:
 
     def __init__(self, inp, device="cuda", backward=True):
         self.inp = inp
-        self.dm = moe.dims(inp.T, inp.d, inp.f, inp.E, inp.k)
-        self.x = bf16_dev(inp.x, device)
-        self.W1 = bf16_dev(inp.W1, device)
-        self.W2 = bf16_dev(inp.W2, device)
+        self.fp8 = inp.dtype == "fp8"
+        self.dm = moe.dims(inp.T, inp.d, inp.f, inp.E, inp.k, moe.MOE_FP8_E4M3 if self.fp8 else moe.MOE_BF16)
+        if self.fp8:
+            self.x, self.W1, self.W2 = (torch.from_numpy(np.ascontiguousarray(a)).to(device)
+                                        for a in (inp.x, inp.W1, inp.W2))
+            self.x_scale, self.W1_scale, self.W2_scale = (torch.from_numpy(np.ascontiguousarray(a)).to(device)
+                                                          for a in (inp.x_scale, inp.W1_scale, inp.W2_scale))
+        else:
+            self.x = bf16_dev(inp.x, device)
+            self.W1 = bf16_dev(inp.W1, device)
+            self.W2 = bf16_dev(inp.W2, device)
+            self.x_scale = self.W1_scale = self.W2_scale = None
         self.dy = bf16_dev(inp.dy, device) if (backward and inp.dy is not None) else None
         self.logits = torch.from_numpy(inp.logits).to(device) if inp.logits is not None else None
         self.b = moe.alloc_layer_buffers(self.dm, device, backward=backward and self.dy is not None)
@@ -63,12 +71,13 @@ class GpuLayer:
 
     def forward(self):
         b = self.b
-        moe.moe_forward(self.dm, self.x, None, self.W1, None, self.W2, None, b["topk_w"], b["offsets"], b["perm"],
-                        b["inv_perm"], b["y"], b["saved"], b["ws_fwd"])
+        moe.moe_forward(self.dm, self.x, self.x_scale, self.W1, self.W1_scale, self.W2, self.W2_scale, b["topk_w"],
+                        b["offsets"], b["perm"], b["inv_perm"], b["y"], b["saved"], b["ws_fwd"])
 
     def backward(self, with_logits=True):
         b = self.b
-        moe.moe_backward(self.dm, self.dy, self.x, None, self.W1, None, self.W2, None, b["topk_ids"], b["topk_w"],
+        moe.moe_backward(self.dm, self.dy, self.x, self.x_scale, self.W1, self.W1_scale, self.W2, self.W2_scale,
+                         b["topk_ids"], b["topk_w"],
                          b["offsets"], b["perm"], b["inv_perm"], b["saved"], b["dx"], b["dW1"], b["dW2"],
                          b["d_topk_w"], b["d_logits"] if with_logits else None, b["ws_bwd"])
 
@@ -89,9 +98,15 @@ class GpuLayer:
 
 
 def oracle_inputs(inp):
-    x = oracle.bf16_to_f64(inp.x)
-    W1 = oracle.bf16_to_f64(inp.W1)
-    W2 = oracle.bf16_to_f64(inp.W2)
+    """fp64 copies of the layer inputs; fp8 operands are dequantised exactly (codes times scales)."""
+    if inp.dtype == "fp8":
+        x = oracle.dequant_rows_1x128(inp.x, inp.x_scale)
+        W1 = oracle.dequant_blocks_128x128(inp.W1, inp.W1_scale)
+        W2 = oracle.dequant_blocks_128x128(inp.W2, inp.W2_scale)
+    else:
+        x = oracle.bf16_to_f64(inp.x)
+        W1 = oracle.bf16_to_f64(inp.W1)
+        W2 = oracle.bf16_to_f64(inp.W2)
     dy = oracle.bf16_to_f64(inp.dy) if inp.dy is not None else None
     return x, W1, W2, dy
 

@@ -68,6 +68,18 @@ def test_dtype_and_reserved_errors(lib):
     assert sz(lib, moe.dims(64, 128, 256, 8, 2), 3)[0] == moe.MOE_ERR_SHAPE
 
 
+def test_fp8_shape_rules(lib):
+    # the fp8 tiles are 256 wide along d and f
+    assert sz(lib, moe.dims(64, 128, 256, 8, 2, dtype=moe.MOE_FP8_E4M3), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
+    assert sz(lib, moe.dims(64, 256, 384, 8, 2, dtype=moe.MOE_FP8_E4M3), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
+    bf = moe.dims(64, 256, 256, 8, 2)
+    f8 = moe.dims(64, 256, 256, 8, 2, dtype=moe.MOE_FP8_E4M3)
+    # fp8 adds the e4m3 copies of As (forward) and of dy, dH plus bf16 x (backward)
+    A, d, f = 128, 256, 256
+    assert sz(lib, f8, moe.MOE_WS_FORWARD)[1] >= sz(lib, bf, moe.MOE_WS_FORWARD)[1] + A * f + A * (f // 128) * 4
+    assert sz(lib, f8, moe.MOE_WS_BACKWARD)[1] >= sz(lib, bf, moe.MOE_WS_BACKWARD)[1] + 64 * d * 3 + A * 2 * f
+
+
 def test_workspace_sizes_scale_with_pairs_not_capacity(lib):
     small = sz(lib, moe.dims(64, 128, 256, 8, 2), moe.MOE_WS_FORWARD)[1]
     big = sz(lib, moe.dims(128, 128, 256, 8, 2), moe.MOE_WS_FORWARD)[1]
@@ -110,10 +122,18 @@ def test_forward_backward_argument_errors(lib):
     assert fwd(xs=F) == moe.MOE_ERR_DTYPE                 # scales with bf16
     assert fwd(ws=wf - 1) == moe.MOE_ERR_WORKSPACE
     assert fwd(x=F + 2) == moe.MOE_ERR_ALIGN
-    fp8 = moe.dims(64, 128, 256, 8, 2, dtype=moe.MOE_FP8_E4M3)
-    _, wf8 = sz(lib, fp8, moe.MOE_WS_FORWARD)
-    assert lib.moe_forward(ctypes.byref(fp8), F, None, F, F, F, F, F, F, F, F, F, F, F, wf8, None) in (
-        moe.MOE_ERR_DTYPE, moe.MOE_ERR_NULL)               # fp8 needs every scale
+    fp8 = moe.dims(64, 256, 256, 8, 2, dtype=moe.MOE_FP8_E4M3)
+    rc, wf8 = sz(lib, fp8, moe.MOE_WS_FORWARD)
+    assert rc == 0
+    f8 = lambda *sc, ws=wf8: lib.moe_forward(ctypes.byref(fp8), F, sc[0], F, sc[1], F, sc[2], F, F, F, F, F, F, F,
+                                             ws, None)
+    assert f8(None, F, F) == moe.MOE_ERR_NULL              # fp8 needs every scale
+    assert f8(F, F, None) == moe.MOE_ERR_NULL
+    assert f8(F, F, F, ws=wf8 - 1) == moe.MOE_ERR_WORKSPACE
+    assert f8(F + 4, F, F) == moe.MOE_ERR_ALIGN
+    b8 = lambda *sc: lib.moe_backward(ctypes.byref(fp8), F, F, sc[0], F, sc[1], F, sc[2], F, F, F, F, F, F, F, F, F,
+                                      F, F, F, sz(lib, fp8, moe.MOE_WS_BACKWARD)[1], None)
+    assert b8(F, None, F) == moe.MOE_ERR_NULL
     bwd = lambda **o: lib.moe_backward(ctypes.byref(dm), F, F, None, F, None, F, None, o.get("ids", F), F, F, F, F, F,
                                        F, F, F, o.get("dtw", F), o.get("dl", F), F, o.get("ws", wb), None)
     assert bwd(dtw=None) == moe.MOE_ERR_NULL
