@@ -1,44 +1,84 @@
 #!/usr/bin/env python3
-"""Benchmark of the dropless MoE layer (route + forward + backward) on one MI355X.
+"""Benchmark of the dropless MoE layer (route or plan + forward + backward) on one MI355X.
 
-One step = moe_route + moe_forward + moe_backward over one batch of seeded synthetic inputs
-already resident in HBM.  Prints one JSON line (the benchmark contract) with useful TFLOPS
-(18 * routed_pairs * d * f flop per step), tokens/s, the fraction of the dense bf16 MFMA peak,
-a roofline entry for the dominant kernel (average duration from HIP stream events recorded
-around every kernel launch during the timed steps), and the fp64 CPU oracle timed on a bounded
-sample of the same workload on the host cores.
+One step = moe_route (moe_plan for pre-routed input) + moe_forward + moe_backward over one
+batch of seeded synthetic inputs already resident in HBM.  Prints one JSON line with useful
+TFLOPS (18 * routed_pairs * d * f flop per step), tokens/s, the fraction of the dense MFMA
+peak, a roofline entry for the dominant kernel (average duration from HIP events recorded on
+the launch stream around every kernel during the timed steps; HBM traffic from committed
+rocprofv3 counter summaries when they match the current kernel sources) and the fp64 CPU
+oracle timed on a bounded sample of the same workload on the host cores.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config qwen3] [--no-cpu-baseline]
+
+Helpers that read rocprofv3 CSV output (CPU only, print a text summary):
+
+    python bench.py --summarize-stats DIR --config C --command "..."
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR --config C --command "..."
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "MoE layer fwd+bwd useful TFLOPS and tokens/s on 1 MI355X; % MFMA peak"
-PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+# MI355X dense MFMA peaks: 256 CU x 2.4 GHz x (4096 bf16 | 8192 fp8) flop per CU-clock
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+CALIB_MIB = 1024              # size of the copy kernel that calibrates the HBM byte counters
 
 WORKLOADS = {
     "qwen3": "Qwen3-30B-A3B-shaped MoE layer fwd+bwd: T=16384, d=2048, f=768, E=128, top-8, bf16",
     "skewed": "Qwen3-30B-A3B-shaped MoE layer fwd+bwd with Zipf-skewed routing (bias 3*ln(1/rank)), bf16",
     "mixtral": "Mixtral-8x7B-shaped MoE layer fwd+bwd: T=8192, d=4096, f=14336, E=8, top-2, bf16",
+    "dsv3_fp8": ("DeepSeek-V3-shaped single-GPU expert share fwd+bwd: 32 of 256 experts, 8x4096 tokens "
+                 "pre-routed top-8, d=7168, f=2048, e4m3 with fp32 block scales, bf16 outputs"),
     "tiny": "tiny MoE layer: T=64, d=128, f=256, E=8, top-2, bf16",
 }
 
-# stage -> (flop per routed pair as a multiple of d*f) for the grouped GEMMs
+# stage -> flop per routed pair as a multiple of d*f, for the grouped GEMMs
 GEMM_FLOP_PER_PAIR = {"gemm_up": 4, "gemm_down": 2, "gemm_dact": 2, "gemm_dx": 4, "gemm_dw2": 2, "gemm_dw1": 4}
+# stage -> (kernel symbol prefix) as it appears in rocprofv3 output
+STAGE_KERNEL_BF16 = {"gemm_up": "moe::grouped_gemm_kernel<0,", "gemm_down": "moe::grouped_gemm_kernel<1,",
+                     "gemm_dact": "moe::grouped_gemm_kernel<2,", "gemm_dx": "moe::grouped_gemm_kernel<3,",
+                     "gemm_dw2": "moe::grouped_gemm_kernel<4,", "gemm_dw1": "moe::grouped_gemm_kernel<5,",
+                     "combine": "moe::combine_kernel", "router": "moe::router_topk_kernel",
+                     "dlogits": "moe::dlogits_kernel", "wg_reduce": "moe::wg_reduce_kernel",
+                     "plan": "moe::plan_", "tile_map": "moe::tile_map_kernel", "wg_split": "moe::wg_split_kernel",
+                     "tokrow": "moe::tokrow_kernel"}
+STAGE_KERNEL_FP8 = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_fp8_kernel<0>",
+                        gemm_down="moe::grouped_gemm_fp8_kernel<1>", gemm_dact="moe::grouped_gemm_fp8_kernel<2>",
+                        gemm_dx="moe::grouped_gemm_fp8_kernel<3>", quant_dy="moe::quant_rows_kernel",
+                        dequant_x="moe::dequant_rows_kernel")
+FP8_STAGES = ("gemm_up", "gemm_down", "gemm_dact", "gemm_dx")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def is_fp8(config):
+    return config.endswith("fp8")
+
+
+def stage_dtype(config, stage):
+    return "fp8" if (is_fp8(config) and stage in FP8_STAGES) else "bf16"
+
+
+def stage_kernels(config):
+    return STAGE_KERNEL_FP8 if is_fp8(config) else STAGE_KERNEL_BF16
+
+
 def stage_bytes(stage, T, d, f, E, k, A):
-    """Algorithmic HBM bytes of one launch of a bandwidth-bound stage."""
+    """Algorithmic HBM bytes of one launch of a bandwidth-bound stage (each byte the stage
+    must read or write once; A = routed pairs)."""
     if stage in ("combine", "combine_dx"):
         return A * d * 2 + T * d * 2 + T * k * 4
     if stage == "router":
@@ -47,39 +87,178 @@ def stage_bytes(stage, T, d, f, E, k, A):
         return A * 4 * 3
     if stage == "dlogits":
         return T * k * 4 * 3 + T * E * 4
+    if stage == "quant_dy":
+        return T * d * 2 + T * d + T * (d // 128) * 4
+    if stage == "dequant_x":
+        return T * d + T * (d // 128) * 4 + T * d * 2
     return None
 
 
-def cpu_baseline(inp, n_tokens: int):
-    """The fp64 oracle (route, plan, forward, backward) on the first n_tokens tokens."""
+def kernel_source_hash():
+    """Hash of every kernel and ABI source; a stored counter summary is only used while it matches."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "grouped_gemm_expert_router_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(config):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{config}.txt")
+
+
+def stored_traffic(config, stage):
+    """HBM bytes per launch of `stage` (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel
+    calibration) from the committed counter summary, or None if absent or stale."""
+    path = traffic_file(config)
+    if not os.path.exists(path):
+        return None
+    rec, src = {}, None
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("source_hash:"):
+                src = line.split(":", 1)[1].strip()
+            elif line.startswith("stage "):
+                parts = dict(kv.split("=", 1) for kv in line.split()[2:])
+                rec[line.split()[1]] = float(parts["traffic_bytes"])
+    if src != kernel_source_hash():
+        return None
+    return rec.get(stage)
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def _host_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(inp, target_s: float):
+    """The fp64 oracle (route or plan, forward, backward) on the first n tokens, with n grown
+    from 256 until one timed run takes at least half of target_s (the last run is reported)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
     import oracle
-    try:
-        ncores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncores = os.cpu_count() or 1
-    ncores = max(1, min(16, ncores))
-    n = min(n_tokens, inp.T)
-    x = oracle.bf16_to_f64(inp.x[:n])
-    dy = oracle.bf16_to_f64(inp.dy[:n])
-    W1 = oracle.bf16_to_f64(inp.W1)
-    W2 = oracle.bf16_to_f64(inp.W2)
-    L = inp.logits[:n]
+    ncores = _host_cores()
+    fp8 = inp.dtype == "fp8"
+    if fp8:
+        x_all = oracle.dequant_rows_1x128(inp.x, inp.x_scale)
+        W1 = np.empty(inp.W1.shape, np.float64)
+        W2 = np.empty(inp.W2.shape, np.float64)
+        for e in range(inp.E):      # one expert at a time bounds the temporaries
+            W1[e] = oracle.dequant_blocks_128x128(inp.W1[e], inp.W1_scale[e])
+            W2[e] = oracle.dequant_blocks_128x128(inp.W2[e], inp.W2_scale[e])
+    else:
+        x_all = None
+        W1 = oracle.bf16_to_f64(inp.W1)
+        W2 = oracle.bf16_to_f64(inp.W2)
+
+    def run(n):
+        x = x_all[:n] if fp8 else oracle.bf16_to_f64(inp.x[:n])
+        dy = oracle.bf16_to_f64(inp.dy[:n])
+        t0 = time.perf_counter()
+        if fp8:
+            ids, w = inp.topk_ids[:n], inp.topk_w[:n].astype(np.float64)
+            oracle.plan(ids, inp.E)
+        else:
+            ids, w = oracle.route(inp.logits[:n], inp.k)
+            oracle.plan(ids, inp.E)
+        oracle.forward(x, W1, W2, ids, w, E=inp.E)
+        oracle.backward(x, W1, W2, ids, w, dy, logits_routed=not fp8)
+        dt = time.perf_counter() - t0
+        pairs = int((ids >= 0).sum())
+        return dt, pairs
+
     with threadpool_limits(limits=ncores):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        t0 = time.perf_counter()
-        ids, w = oracle.route(L, inp.k)
-        oracle.forward(x, W1, W2, ids, w)
-        oracle.backward(x, W1, W2, ids, w, dy)
-        dt = time.perf_counter() - t0
-    A = n * inp.k
-    return {"value": 18.0 * A * inp.d * inp.f / dt / 1e12, "unit": "TFLOPS", "cores": int(threads),
+        # the oracle's per-expert loop has a fixed cost, so grow the sample until it is long enough
+        n = min(inp.T, 256)
+        for _ in range(5):
+            dt, pairs = run(n)
+            if dt >= 0.5 * target_s or n >= inp.T:
+                break
+            n = int(min(inp.T, max(2 * n, n * target_s / max(dt, 1e-3))))
+    return {"value": 18.0 * pairs * inp.d * inp.f / dt / 1e12, "unit": "TFLOPS", "cores": int(threads),
             "kind": "oracle", "tokens_per_s": n / dt, "seconds": dt,
-            "sample": f"first {n} of {inp.T} tokens of the same workload (all {inp.E} experts), "
-                      f"route+plan+forward+backward in fp64 numpy, {threads} BLAS threads"}
+            "sample": f"first {n} of {inp.T} tokens of the same workload ({pairs} routed pairs, all {inp.E} "
+                      f"experts), {'plan' if fp8 else 'route+plan'}+forward+backward in fp64 numpy on "
+                      f"{'exactly dequantised fp8 inputs' if fp8 else 'bf16 inputs'}, {threads} BLAS threads"}
 
 
+# ------------------------------------------------------------------ rocprofv3 summaries
+def _csv_rows(d, suffix):
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for p in files:
+        with open(p, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _stage_of(name, config):
+    for st, pre in stage_kernels(config).items():
+        if pre in name:
+            return st
+    return None
+
+
+def summarize_stats(d, config, command):
+    rows = _csv_rows(d, "kernel_stats.csv")
+    print(f"# rocprofv3 kernel statistics: {WORKLOADS[config]}")
+    print(f"command: {command}")
+    print(f"source_hash: {kernel_source_hash()}")
+    print(f"{'stage':<12} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}  kernel")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        st = _stage_of(r["Name"], config) or "-"
+        print(f"{st:<12} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} {float(r['MinNs']) / 1e3:>10.1f} "
+              f"{float(r['MaxNs']) / 1e3:>10.1f} {float(r['Percentage']):>7.2f}  {r['Name'][:110]}")
+
+
+def summarize_counters(fetch_dir, write_dir, config, command):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) per kernel, scaled by what the same counters
+    read for the calibration copy (torch.neg over CALIB_MIB MiB of fp32: that many bytes read
+    and written)."""
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = CALIB_MIB * 2 ** 20
+
+    def calib(acc, what):
+        ks = [k for k in acc if "neg_kernel" in k]
+        if not ks:
+            raise SystemExit(f"calibration copy kernel not found among {what} dispatches")
+        v = sorted(acc[ks[0]])[len(acc[ks[0]]) // 2] * 1024.0
+        return copy_bytes / v
+    ff, fw = calib(fetch, "FETCH_SIZE"), calib(write, "WRITE_SIZE")
+    print(f"# rocprofv3 HBM byte counters per dispatch: {WORKLOADS[config]}")
+    print(f"command: {command}")
+    print(f"source_hash: {kernel_source_hash()}")
+    print(f"calibration: torch.neg over {CALIB_MIB} MiB fp32 -> fetch_factor={ff:.4f} write_factor={fw:.4f}")
+    print("# stage <name> kernel=<symbol> fetch_kib=<median raw> write_kib=<median raw> traffic_bytes=<scaled sum>")
+    for name in sorted(set(fetch) & set(write)):
+        st = _stage_of(name, config)
+        if st is None:
+            continue
+        fk = sorted(fetch[name])[len(fetch[name]) // 2]
+        wk = sorted(write[name])[len(write[name]) // 2]
+        tb = fk * 1024.0 * ff + wk * 1024.0 * fw
+        print(f"stage {st} fetch_kib={fk:.1f} write_kib={wk:.1f} traffic_bytes={tb:.0f} "
+              f"kernel={name.split('(')[0].replace(' ', '')}")
+
+
+# ------------------------------------------------------------------ benchmark
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,8 +266,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help=f"run a {CALIB_MIB} MiB copy kernel first (calibrates profiler byte counters)")
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--command", default="", help="profiler command recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats, args.config, args.command)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters, args.config, args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this layer is one GPU's share of an expert-parallel "
               f"layer and the build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -104,39 +292,65 @@ def main():
     t_gen = time.perf_counter()
     inp = make_config(args.config)
     log(f"[bench] generated {args.config} inputs in {time.perf_counter() - t_gen:.1f}s")
+    fp8 = inp.dtype == "fp8"
     T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
-    dm = moe.dims(T, d, f, E, k)
+    dm = moe.dims(T, d, f, E, k, moe.MOE_FP8_E4M3 if fp8 else moe.MOE_BF16)
     dev = "cuda"
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    x, W1, W2, dy = bf16(inp.x), bf16(inp.W1), bf16(inp.W2), bf16(inp.dy)
-    logits = torch.from_numpy(inp.logits).to(dev)
+    def raw(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if fp8:
+        x, W1, W2 = raw(inp.x), raw(inp.W1), raw(inp.W2)
+        xs, W1s, W2s = raw(inp.x_scale), raw(inp.W1_scale), raw(inp.W2_scale)
+        logits = None
+    else:
+        x, W1, W2 = bf16(inp.x), bf16(inp.W1), bf16(inp.W2)
+        xs = W1s = W2s = None
+        logits = torch.from_numpy(inp.logits).to(dev)
+    dy = bf16(inp.dy)
     b = moe.alloc_layer_buffers(dm, dev, backward=True)
+    if fp8:
+        b["topk_ids"].copy_(torch.from_numpy(inp.topk_ids))
+        b["topk_w"].copy_(torch.from_numpy(inp.topk_w))
     torch.cuda.synchronize()
 
+    if args.calibrate_copy:
+        src = torch.ones(CALIB_MIB * 2 ** 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     def step():
-        moe.moe_route(dm, logits, b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["perm"], b["inv_perm"],
-                      b["ws_route"])
-        moe.moe_forward(dm, x, None, W1, None, W2, None, b["topk_w"], b["offsets"], b["perm"], b["inv_perm"], b["y"],
+        if fp8:
+            moe.moe_plan(dm, b["topk_ids"], b["counts"], b["offsets"], b["perm"], b["inv_perm"], b["ws_route"])
+        else:
+            moe.moe_route(dm, logits, b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["perm"],
+                          b["inv_perm"], b["ws_route"])
+        moe.moe_forward(dm, x, xs, W1, W1s, W2, W2s, b["topk_w"], b["offsets"], b["perm"], b["inv_perm"], b["y"],
                         b["saved"], b["ws_fwd"])
-        moe.moe_backward(dm, dy, x, None, W1, None, W2, None, b["topk_ids"], b["topk_w"], b["offsets"], b["perm"],
-                         b["inv_perm"], b["saved"], b["dx"], b["dW1"], b["dW2"], b["d_topk_w"], b["d_logits"],
-                         b["ws_bwd"])
+        moe.moe_backward(dm, dy, x, xs, W1, W1s, W2, W2s, b["topk_ids"], b["topk_w"], b["offsets"], b["perm"],
+                         b["inv_perm"], b["saved"], b["dx"], b["dW1"], b["dW2"], b["d_topk_w"],
+                         None if fp8 else b["d_logits"], b["ws_bwd"])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    # per-kernel stream events around every launch inside the timed steps
-    events = []
-    open_ev = {}
+    # HIP events on the launch stream around every kernel of the timed steps
+    cur = torch.cuda.current_stream()
+    events, open_ev = [], {}
 
     def hook(stage, begin, stream_ptr):
+        assert (stream_ptr or 0) == (cur.cuda_stream or 0), "kernel launched on another stream"
         ev = torch.cuda.Event(enable_timing=True)
-        ev.record()
+        ev.record(cur)
         if begin:
             open_ev[stage] = ev
         else:
@@ -145,10 +359,10 @@ def main():
     moe.moe_set_stage_hook(hook)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
+    start.record(cur)
     for _ in range(args.steps):
         step()
-    stop.record()
+    stop.record(cur)
     torch.cuda.synchronize()
     moe.moe_set_stage_hook(None)
     ms = start.elapsed_time(stop) / args.steps
@@ -161,13 +375,16 @@ def main():
     for stage, e0, e1 in events:
         per.setdefault(stage, []).append(e0.elapsed_time(e1))
     stages = {}
+    ideal_ms = 0.0   # time of the GEMMs at their dtype's MFMA peak
     for stage, ts in per.items():
         avg = sum(ts) / len(ts)
         ent = {"launches": len(ts), "avg_ms": avg, "ms_per_step": sum(ts) / args.steps}
         if stage in GEMM_FLOP_PER_PAIR:
             fl = GEMM_FLOP_PER_PAIR[stage] * A * d * f
-            ent["tflops"] = fl / (avg * 1e-3) / 1e12
-            ent["frac_mfma_peak"] = ent["tflops"] / PEAK_BF16_TFLOPS
+            pk = PEAK_TFLOPS[stage_dtype(args.config, stage)]
+            ent.update(dtype=stage_dtype(args.config, stage), tflops=fl / (avg * 1e-3) / 1e12)
+            ent["frac_mfma_peak"] = ent["tflops"] / pk
+            ideal_ms += fl / (pk * 1e12) * 1e3
         else:
             by = stage_bytes(stage, T, d, f, E, k, A)
             if by:
@@ -177,32 +394,36 @@ def main():
                                            sorted(stages.items(), key=lambda kv: -kv[1]["ms_per_step"])))
     dom = max(stages, key=lambda s: stages[s]["ms_per_step"])
     dom_e = stages[dom]
+    traffic = stored_traffic(args.config, dom)
     if dom in GEMM_FLOP_PER_PAIR:
         fl = GEMM_FLOP_PER_PAIR[dom] * A * d * f
+        pk = PEAK_TFLOPS[stage_dtype(args.config, dom)]
         achieved = fl / (dom_e["avg_ms"] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "algorithmic_flop_per_launch": fl,
-                "avg_launch_ms": dom_e["avg_ms"]}
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": pk, "unit": "TFLOP/s",
+                "frac": achieved / pk, "traffic": traffic, "dtype": stage_dtype(args.config, dom),
+                "algorithmic_flop_per_launch": fl, "avg_launch_ms": dom_e["avg_ms"]}
     else:
         by = stage_bytes(dom, T, d, f, E, k, A)
         achieved = by / (dom_e["avg_ms"] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": by,
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": by,
                 "avg_launch_ms": dom_e["avg_ms"]}
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle on {min(args.cpu_tokens, T)} tokens ...")
-        cpu = cpu_baseline(inp, args.cpu_tokens)
+        log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f}s sample) ...")
+        cpu = cpu_baseline(inp, args.cpu_seconds)
         log(f"[bench] CPU oracle: {cpu['seconds']:.1f}s, {cpu['value'] * 1e3:.2f} GFLOPS, {cpu['cores']} threads")
 
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8_e4m3+bf16" if fp8 else "bf16", "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "T": T, "d": d, "f": f, "E": E, "k": k,
                    "routed_pairs": A, "seed_config": args.config},
-        "tokens_per_s": T / (ms * 1e-3), "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "tokens_per_s": T / (ms * 1e-3),
+        "frac_of_bf16_peak": tflops / PEAK_TFLOPS["bf16"],
+        "frac_of_mfma_peak": ideal_ms / ms,
         "useful_flop_per_step": useful, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -26,7 +26,9 @@
 
 namespace moe {
 
-enum GemmMode { M_UP = 0, M_DOWN = 1, M_DACT = 2, M_DX = 3, M_WG = 4 };
+// M_WG and M_WG1 are the same ragged-K weight-gradient kernel (dW2 and dW1), kept as two
+// instantiations so the two launches carry distinct names in kernel traces.
+enum GemmMode { M_UP = 0, M_DOWN = 1, M_DACT = 2, M_DX = 3, M_WG = 4, M_WG1 = 5 };
 
 struct GemmArgs {
   const uint16_t* A;
@@ -64,7 +66,7 @@ template <int MODE, int BM, int BN, int WN, int OCC, int BK>
 __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmArgs g) {
   constexpr int S = BK == 32 ? 4 : 2, WM = 2, NW = WM * WN, NTH = 64 * NW;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr bool RAGGED_K = (MODE == M_WG);
+  constexpr bool RAGGED_K = (MODE == M_WG || MODE == M_WG1);
   constexpr bool A_KN = RAGGED_K;                              // A stored [k][m]
   constexpr bool B_KN = !(MODE == M_DACT || MODE == M_DX);     // B stored [k][n]
   static_assert(MODE != M_UP || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
         for (int m = CH / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
         if (ok && cc == 0) g.dwp[(int64_t)(m0 + lr) * g.nparts + nt] = part;
       }
-    } else if (MODE == M_WG && pslot >= 0) {
+    } else if (RAGGED_K && pslot >= 0) {
       // one chunk of a split expert: fp32 partial, summed later in chunk order
       float* out = g.partial + (int64_t)(pslot + kchunk) * g.Mo * g.N;
       for (int id = tid; id < 64 * CH; id += NTH) {
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
           const uint4 o = make_uint4(pack_bf16x2(cp[0], cp[1]), pack_bf16x2(cp[2], cp[3]),
                                      pack_bf16x2(cp[4], cp[5]), pack_bf16x2(cp[6], cp[7]));
           int64_t orow;
-          if constexpr (MODE == M_WG) orow = (int64_t)e * g.Mo + m0 + lr;
+          if constexpr (RAGGED_K) orow = (int64_t)e * g.Mo + m0 + lr;
           else orow = s_slot[lr];
           *(uint4*)&g.C0[orow * g.ldc0 + n0 + cc * 8] = o;
         }
@@ -461,7 +463,7 @@ hipError_t run(const GemmArgs& g, int bm, int bn, dim3 grid, hipStream_t st) {
     grouped_gemm_kernel<MODE, 256, 256, 4, 1, BKC><<<grid, 512, 0, st>>>(g);
   else if (bm == 256 && bn == 128)
     grouped_gemm_kernel<MODE, 256, 128, (MODE == M_UP ? 2 : 4), 1, BKC><<<grid, (MODE == M_UP ? 256 : 512), 0, st>>>(g);
-  else if (MODE == M_WG && bm == 128 && bn == 256)
+  else if ((MODE == M_WG || MODE == M_WG1) && bm == 128 && bn == 256)
     grouped_gemm_kernel<MODE, 128, 256, 4, 1, BKC><<<grid, 512, 0, st>>>(g);
   else if (bm == 128 && bn == 128)
     grouped_gemm_kernel<MODE, 128, 128, 2, 2, 32><<<grid, 256, 0, st>>>(g);
@@ -719,7 +721,7 @@ hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t*
   g.ldc0 = 2 * (int64_t)s.f;
   const int bm = pick_bn(s.d), bn = pick_bn(2 * s.f);
   dim3 grid((unsigned)((s.d / bm) * (2 * s.f / bn) * (s.E + sp.max_partials)));
-  return run<M_WG>(g, bm, bn, grid, st);
+  return run<M_WG1>(g, bm, bn, grid, st);
 }
 
 }  // namespace moe
