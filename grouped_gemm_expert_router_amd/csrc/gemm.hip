@@ -102,17 +102,38 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     const int nN = g.N / BN;
     const int per_u = (g.Mo / BM) * nN;
     const CONST_AS int32_t* meta = (const CONST_AS int32_t*)g.wg_meta;
-    const int G_valid = meta[0] * per_u;
+    const int U = meta[0];
+    const int G_valid = U * per_u;
     if ((int)blockIdx.x >= G_valid) return;  // uniform: the block has no work
-    // Units are in decreasing size and blocks go round-robin to the XCDs, so every XCD gets an
-    // equal share of each unit; within a unit the dimension with 8 tiles runs fastest, so an
-    // XCD's share of a unit reuses one operand slice.
-    const int lid = blockIdx.x;
-    const int u = lid / per_u;
+    // Units come in decreasing size.  Deal them to 8 buckets round-robin (bucket b holds units
+    // b, b+8, ...: near-equal work per bucket) and give XCD b the tiles of bucket b, so each
+    // XCD streams its units' operand rows from HBM into its own L2 once instead of every XCD
+    // re-reading every unit.  The logical order is bucket-major, cut into 8 equal tile ranges
+    // by xcd_remap, which also spreads the tiles when there are fewer than 8 units.
+    // When that leaves the buckets uneven (a few long units), the split kernel clears meta[2]
+    // and blocks take the units in order instead: the round-robin dispatch then hands every
+    // XCD an equal share of each unit.
+    int pos = blockIdx.x, u;
+    if (meta[2]) {
+      pos = xcd_remap(blockIdx.x, G_valid);
+      const int j = pos / per_u;
+      const int q = U / 8, r = U % 8;
+      int b, jb;
+      if (j < r * (q + 1)) {
+        b = j / (q + 1);
+        jb = j % (q + 1);
+      } else {
+        b = r + (j - r * (q + 1)) / q;
+        jb = (j - r * (q + 1)) % q;
+      }
+      u = b + 8 * jb;
+    } else {
+      u = pos / per_u;
+    }
     const CONST_AS int32_t* up = (const CONST_AS int32_t*)g.wg_units;
     e = up[2 * u];
     kchunk = up[2 * u + 1];
-    const int t = lid % per_u, nM = g.Mo / BM;
+    const int t = pos % per_u, nM = g.Mo / BM;
     if (nM % 8 == 0 || nN % 8 != 0) {
       m0 = (t % nM) * BM;
       nt = t / nM;
@@ -610,6 +631,7 @@ __global__ __launch_bounds__(1024) void wg_split_kernel(const int32_t* __restric
   // round-robin over XCDs spreads them evenly.
   __shared__ int2 s_unit[2048];
   __shared__ int s_rows[2048];
+  __shared__ int s_sorted[2048];  // rows of the unit at each position of the written order
   if (e < E) {
     pslot[e] = split ? pbase : -1;
     for (int ch = 0; ch < nch; ++ch) {
@@ -626,10 +648,27 @@ __global__ __launch_bounds__(1024) void wg_split_kernel(const int32_t* __restric
       rank += (rj > ri) || (rj == ri && j < i);
     }
     units[rank] = s_unit[i];
+    s_sorted[rank] = ri;
   }
+  // Rows per XCD bucket (units b, b+8, ... in the order just written); the bucketed tile order
+  // is used only when the fullest bucket is within 1/32 of the mean.
+  __syncthreads();
+  __shared__ int s_bucket[8];
+  if (threadIdx.x < 8) {
+    int rows = 0;
+    for (int i = threadIdx.x; i < total; i += 8) rows += s_sorted[i];
+    s_bucket[threadIdx.x] = rows;
+  }
+  __syncthreads();
   if (e == 0) {
+    int mx = 0, sum = 0;
+    for (int b = 0; b < 8; ++b) {
+      mx = max(mx, s_bucket[b]);
+      sum += s_bucket[b];
+    }
     meta[0] = total;
     meta[1] = KC;
+    meta[2] = (int64_t)mx * 8 * 32 <= (int64_t)sum * 33 ? 1 : 0;
   }
   (void)s_flag;
 }

@@ -52,7 +52,7 @@ constexpr int kWgMaxPartials = 32;
 constexpr int64_t kWgPartialBudget = (int64_t)512 << 20;
 struct WgSplit {
   int2* units;       // [E + max_partials]
-  int32_t* meta;     // [2]
+  int32_t* meta;     // [3]: unit count, chunk rows KC, 1 = bucketed XCD tile order
   int32_t* pslot;    // [E]
   float* partial;    // [max_partials, max(d*2f, f*d)]
   const int32_t* offsets;
