@@ -62,6 +62,11 @@ struct GemmArgs {
   float* partial;
 };
 
+// Row tiles per group of the ragged-M tile order (grouped_tile).
+#ifndef GEMM_GM
+#define GEMM_GM 8
+#endif
+
 template <int MODE, int BM, int BN, int WN, int OCC, int BK>
 __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmArgs g) {
   constexpr int S = BK == 32 ? 4 : 2, WM = 2, NW = WM * WN, NTH = 64 * NW;
@@ -153,9 +158,9 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     const int G_valid = *(const CONST_AS int32_t*)g.ntiles * nN;
     if ((int)blockIdx.x >= G_valid) return;  // uniform: the block has no work
     const int lid = xcd_remap(blockIdx.x, G_valid);
-    nt = lid % nN;
-    const int tile = lid / nN;
-    const int2 te = g.tiles[tile];
+    const int2 rc = grouped_tile(lid, G_valid / nN, nN, GEMM_GM);
+    nt = rc.y;
+    const int2 te = g.tiles[rc.x];
     e = te.x;
     m0 = g.offsets[e] + te.y * BM;
     mrows = min(BM, g.offsets[e + 1] - m0);

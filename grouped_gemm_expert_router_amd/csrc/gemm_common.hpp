@@ -23,6 +23,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return x * q + min(x, r) + i;
 }
 
+// Logical tile lid of a grid of nrows row tiles x nN column tiles -> (row tile, column tile),
+// in groups of GM row tiles: consecutive lids walk the rows of a group first and then move to
+// the next column tile, so the tiles an XCD runs together share GM row panels and a few column
+// panels in its L2 instead of streaming every column panel once per row tile.
+__device__ __forceinline__ int2 grouped_tile(int lid, int nrows, int nN, int GM) {
+  const int grp = lid / (GM * nN);
+  const int r0 = grp * GM;
+  const int gsz = min(GM, nrows - r0);
+  const int idx = lid - grp * GM * nN;
+  return make_int2(r0 + idx % gsz, idx / gsz);
+}
+
 // ---------------------------------------------------------------- LDS DMA and barriers
 // global_load_lds_dwordx4 copies each lane's 16 bytes to LDS at m0 + 16*lane.  It is issued
 // through inline asm so the compiler's wait-count pass does not make every LDS read wait for

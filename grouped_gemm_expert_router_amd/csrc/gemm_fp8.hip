@@ -8,7 +8,7 @@
 //
 // One K stage is exactly one 128-wide scale block: the stage's two 64-deep MFMAs accumulate
 // into a temporary, which is then promoted into the fp32 accumulator with s_a(row) * s_b(block).
-// Tiles are 128 x 256 x 128 with 8 waves (2 x 4), each owning 64 x 64.  Operands reach LDS by
+// Tiles are 256 x 256 x 128 with 8 waves (2 x 4), each owning 128 x 64.  Operands reach LDS by
 // DMA; K-contiguous tiles are read with ds_read_b128, N-contiguous weight tiles with the 8-bit
 // LDS transpose read.  The row scales of each stage arrive by DMA as well.
 //
@@ -23,6 +23,12 @@
 namespace moe {
 
 enum Fp8Mode { F_UP = 0, F_DOWN = 1, F_DACT = 2, F_DX = 3 };
+
+// Row tiles per group of the tile order (grouped_tile): the large weight panels of the fp8
+// shapes are reused across this many row tiles while they sit in L2.
+#ifndef FP8_GM
+#define FP8_GM 8
+#endif
 
 struct Fp8Args {
   const uint8_t* A;        // fp8 rows, K contiguous
@@ -119,7 +125,7 @@ __device__ __forceinline__ u32x2 quant8_group16(const float (&v)[8], float* scal
 
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args g) {
-  constexpr int BM = 128, BN = 256, BK = 128, S = 2, WM = 2, WN = 4, NW = 8, NTH = 512;
+  constexpr int BM = kFp8BM, BN = 256, BK = 128, S = 2, WM = 2, WN = 4, NW = 8, NTH = 512;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr bool B_KN = (MODE == F_UP || MODE == F_DOWN);
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, SC_BYTES = NW * 256;
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   constexpr int CPAD = BN + 4;
   constexpr int CBAND_BYTES = 2 * 32 * CPAD * 4;
   constexpr int ARENA = S * STAGE > CBAND_BYTES ? S * STAGE : CBAND_BYTES;
-  static_assert(QA == 2 && QB == 4, "DMA split");
+  static_assert(BM == 256 && QA == 4 && QB == 4, "DMA split");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[ARENA];
   float* cband = reinterpret_cast<float*>(smem);
   __shared__ float s_w[BM];
@@ -144,8 +150,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   const int G_valid = *(const CONST_AS int32_t*)g.ntiles * nN;
   if ((int)blockIdx.x >= G_valid) return;
   const int lid = xcd_remap(blockIdx.x, G_valid);
-  const int nt = lid % nN;
-  const int2 te = g.tiles[lid / nN];
+  const int2 rc = grouped_tile(lid, G_valid / nN, nN, FP8_GM);
+  const int nt = rc.y;
+  const int2 te = g.tiles[rc.x];
   const int e = te.x;
   const int m0 = g.offsets[e] + te.y * BM;
   const int mrows = min(BM, g.offsets[e + 1] - m0);
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   const CONST_AS float* Bs = (const CONST_AS float*)g.B_scale + (int64_t)e * g.bs_estride;
 
   // ------------------------------------------------------------------ DMA sources
-  // A (KM, 128 rows x 128 bytes): block gi = 2*wave + q holds rows 8*gi..8*gi+7.
+  // A (KM, 256 rows x 128 bytes): block gi = 4*wave + q holds rows 8*gi..8*gi+7.
   const uint8_t* a_src[QA];
 #pragma unroll
   for (int q = 0; q < QA; ++q) {
@@ -174,10 +181,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
     const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
     a_src[q] = g.A + src * g.lda + 16 * c;
   }
-  // A row scales: wave w brings rows 16w..16w+15 (lanes past 15 repeat row 16w + 15).
+  // A row scales: wave w brings rows 32w..32w+31 (lanes past 31 repeat row 32w + 31).
   const float* sc_src;
   {
-    const int row = 16 * wave + min(lane, 15);
+    const int row = 32 * wave + min(lane, 31);
     const int pos = m0 + (row < mrows ? row : 0);
     const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
     sc_src = g.A_scale + src * g.lds_a;
@@ -233,29 +240,19 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // One K stage = one 128-wide scale block: per 32-row fragment i, two 64-deep MFMAs per B
+  // fragment into a temporary, then acc += temp * s_a(row) * s_b(block).  Row-fragment-major
+  // order keeps only FN temporaries live next to the accumulators.
   auto compute = [&](int st, int kb) __attribute__((always_inline)) {
     const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, sbase = bbase + B_BYTES;
-    f32x16_t t[FM][FN];
+    i32x8 bv[2][FN];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      i32x8 af[FM], bv[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = read_km8(abase, wm * TM + i * 32 + (lane & 31), kk, lane);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if constexpr (B_KN) bv[j] = read_kn8(bbase, b_row(j), kk, lane);
-        else bv[j] = read_km8(bbase, b_row(j) + (lane & 31), kk, lane);
+        if constexpr (B_KN) bv[kk][j] = read_kn8(bbase, b_row(j), kk, lane);
+        else bv[kk][j] = read_km8(bbase, b_row(j) + (lane & 31), kk, lane);
       }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const f32x16_t z = {};
-          t[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bv[j], kk == 0 ? z : t[i][j], 0, 0, 0,
-                                                                     127, 0, 127);
-        }
-    }
-    // promote: acc += t * s_a(row) * s_b(block of the fragment's columns)
     float sb[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -264,20 +261,42 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      const int arow = wm * TM + i * 32 + (lane & 31);
+      f32x16_t t[FN];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const i32x8 af = read_km8(abase, arow, kk, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const f32x16_t z = {};
+          t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bv[kk][j], kk == 0 ? z : t[j], 0, 0, 0, 127, 0,
+                                                                 127);
+        }
+      }
       float sa[16];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = wm * TM + i * 32 + 8 * rr + 4 * (lane >> 5);  // 4 consecutive rows
-        const f32x4_t v = *(const LDS_AS f32x4_t*)(uintptr_t)(sbase + (row >> 4) * 256 + (row & 15) * 4);
+        const f32x4_t v = *(const LDS_AS f32x4_t*)(uintptr_t)(sbase + (row >> 5) * 256 + (row & 31) * 4);
         sa[4 * rr] = v[0];
         sa[4 * rr + 1] = v[1];
         sa[4 * rr + 2] = v[2];
         sa[4 * rr + 3] = v[3];
       }
+      if constexpr (MODE == F_UP) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[i][j][r], sa[r] * sb[j], acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[j][r], sa[r] * sb[j], acc[i][j][r]);
+      } else {
+        // the wave's FN fragments lie in one 128-column block: one s_b
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s2 = sa[r] * sb[0];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j][r] = fmaf(t[j][r], s2, acc[i][j][r]);
+        }
+      }
     }
   };
 

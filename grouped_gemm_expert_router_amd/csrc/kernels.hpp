@@ -74,7 +74,7 @@ hipError_t launch_tokrow(const int32_t* perm, const int32_t* offsets, int E, int
 // fp8 (OCP e4m3) grouped GEMMs with fp32 block scales: activations [rows, K/128] (one scale per
 // row per 128 values), weights [E, rows/128, cols/128] of each matrix as stored.  Row tiles are
 // kFp8BM high; d and f must be multiples of 256.
-constexpr int kFp8BM = 128;
+constexpr int kFp8BM = 256;
 // H = x[perm/k] . W1[e]; As = w * silu(gate) * up in bf16 and as e4m3 + scales [A, f/128].
 hipError_t launch_fp8_up(const MoeShape& s, const uint8_t* x, const float* xs, const uint8_t* W1, const float* W1s,
                          const float* topk_w, const int32_t* offsets, const int32_t* perm, const int2* tiles,
