@@ -62,6 +62,22 @@ struct GemmArgs {
   float* partial;
 };
 
+// Scheduling order for one k step: NM MFMAs, each followed by its share of NRD LDS reads.
+template <int NM, int NRD>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (NM > 0) {
+    constexpr int r = (NRD + NM - 1) / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // r LDS reads
+    sched_interleave<NM - 1, NRD - r>();
+  }
+}
+
+// 1: interleave the next k step's LDS reads with the current MFMAs by scheduling barriers.
+#ifndef GEMM_SCHED
+#define GEMM_SCHED 1
+#endif
+
 // Row tiles per group of the ragged-M tile order (grouped_tile).
 #ifndef GEMM_GM
 #define GEMM_GM 8
@@ -297,26 +313,39 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  auto load_frags = [&](uint32_t abase, uint32_t bbase, int kk, bf16x8_t (&af)[FM], bf16x8_t (&bv)[FN])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (A_KN) af[i] = read_kn<BM>(abase, wm * TM + i * 32, kk, lane);
+      else af[i] = read_km<BK>(abase, wm * TM + i * 32 + (lane & 31), 2 * kk + (lane >> 5));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (B_KN) bv[j] = read_kn<BN>(bbase, b_row(j), kk, lane);
+      else bv[j] = read_km<BK>(bbase, b_row(j) + (lane & 31), 2 * kk + (lane >> 5));
+    }
+  };
+  // The fragments of k step kk+1 are read from LDS while the MFMAs of step kk run (two register
+  // sets); the scheduling barriers keep each read next to an MFMA instead of just before its use.
   auto compute = [&](int st) __attribute__((always_inline)) {
     const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES;
+    constexpr int KS = BK / 16;
+    bf16x8_t af[2][FM], bv[2][FN];
+    load_frags(abase, bbase, 0, af[0], bv[0]);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[FM], bv[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        if constexpr (A_KN) af[i] = read_kn<BM>(abase, wm * TM + i * 32, kk, lane);
-        else af[i] = read_km<BK>(abase, wm * TM + i * 32 + (lane & 31), 2 * kk + (lane >> 5));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (B_KN) bv[j] = read_kn<BN>(bbase, b_row(j), kk, lane);
-        else bv[j] = read_km<BK>(bbase, b_row(j) + (lane & 31), 2 * kk + (lane >> 5));
-      }
+    for (int kk = 0; kk < KS; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KS) load_frags(abase, bbase, kk + 1, af[cur ^ 1], bv[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+#if GEMM_SCHED
+      // LDS read instructions of one step: b128 per KM fragment, two transpose reads per KN one
+      if (kk + 1 < KS) sched_interleave<FM * FN, FM * (A_KN ? 2 : 1) + FN * (B_KN ? 2 : 1)>();
+#endif
     }
   };
 
