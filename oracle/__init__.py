@@ -8,10 +8,12 @@ Every function is pinned by CPU tests against properties the pages and the mathe
 (library sort routines, dense-MLP closed forms, finite differences, conservation identities);
 the pages themselves print no worked values.
 """
-from .formats import bf16_to_f64, e4m3_to_f64, dequant_rows_1x128, dequant_blocks_128x128
+from .formats import (bf16_to_f64, e4m3_to_f64, dequant_rows_1x128, dequant_blocks_128x128, e8m0_to_f64,
+                      e4m3_encode_rne, mx_block_exponent, mx_quantize, mx_dequantize)
 from .moe_ref import (route, plan, Plan, forward, backward, token_forward, token_backward,
                       weight_grad_entries, d_logits_from_dw)
 
-__all__ = ["bf16_to_f64", "e4m3_to_f64", "dequant_rows_1x128", "dequant_blocks_128x128", "route",
+__all__ = ["bf16_to_f64", "e4m3_to_f64", "dequant_rows_1x128", "dequant_blocks_128x128", "e8m0_to_f64",
+           "e4m3_encode_rne", "mx_block_exponent", "mx_quantize", "mx_dequantize", "route",
            "plan", "Plan", "forward", "backward", "token_forward", "token_backward",
            "weight_grad_entries", "d_logits_from_dw"]

@@ -1,0 +1,119 @@
+"""Pins of the oracle's MXFP8 pieces (OCP microscaling: 32-value blocks, e4m3 elements, E8M0
+shared exponents) against the format definition, a library conversion and brute force."""
+from fractions import Fraction
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def test_e8m0_decode():
+    e = np.array([0, 1, 126, 127, 128, 254, 255], np.uint8)
+    got = oracle.e8m0_to_f64(e)
+    np.testing.assert_array_equal(got[:-1], [2.0 ** -127, 2.0 ** -126, 0.5, 1.0, 2.0, 2.0 ** 127])
+    assert np.isnan(got[-1])
+
+
+def test_e4m3_encode_matches_torch_conversion():
+    # torch's float8_e4m3fn cast rounds to nearest even; compare inside the finite range
+    g = np.random.default_rng(0)
+    v = np.concatenate([g.normal(0, 1, 20000), g.normal(0, 100, 20000), g.normal(0, 1e-2, 20000),
+                        g.uniform(-448, 448, 20000)])
+    tab = oracle.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (tab[1:] + tab[:-1]) / 2                      # exact ties between neighbours
+    v = np.concatenate([v, mids, -mids, tab, -tab])
+    v = v[np.abs(v) <= 448]
+    ours = oracle.e4m3_encode_rne(v)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # ties and table values are exact in fp32 (e4m3 has 3 mantissa bits), so the fp32 cast
+    # feeding torch loses nothing
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_encode_roundtrips_every_code_and_saturates():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_encode_rne(oracle.e4m3_to_f64(codes)), codes)
+    assert oracle.e4m3_encode_rne(np.array([1e6]))[0] == 0x7E       # +448
+    assert oracle.e4m3_encode_rne(np.array([-500.0]))[0] == 0xFE     # -448
+
+
+def test_block_exponent_is_smallest_non_clipping_power():
+    g = np.random.default_rng(1)
+    amax = np.concatenate([np.exp(g.uniform(-20, 20, 2000)), 448.0 * np.exp2(np.arange(-10, 10)),
+                           np.nextafter(448.0 * np.exp2(np.arange(-10, 10)), np.inf)])
+    s = oracle.mx_block_exponent(amax)
+    for a, si in zip(amax, s):
+        fa = Fraction(float(a))
+        assert fa <= 448 * Fraction(2) ** int(si)            # fits
+        assert not fa <= 448 * Fraction(2) ** (int(si) - 1)  # and one power less would not
+    assert oracle.mx_block_exponent(np.array([0.0]))[0] == 0
+
+
+def _brute_force_quantize(v):
+    """Per 32-block: s from the definition (math.log2 checked exactly), then each element the
+    e4m3 code minimising |v - value(code) 2^s|, ties to the even code."""
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = oracle.e4m3_to_f64(finite)
+    codes = np.zeros(v.shape, np.uint8)
+    scales = np.zeros(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    for idx in np.ndindex(v.shape[:-1]):
+        for b in range(v.shape[-1] // 32):
+            blk = v[idx][32 * b:32 * b + 32]
+            a = np.abs(blk).max()
+            if a == 0:
+                s = 0
+            else:
+                s = math.ceil(math.log2(a / 448))
+                while Fraction(float(a)) > 448 * Fraction(2) ** s:
+                    s += 1
+                while Fraction(float(a)) <= 448 * Fraction(2) ** (s - 1):
+                    s -= 1
+            scales[idx + (b,)] = s + 127
+            for t, x in enumerate(blk):
+                err = np.abs(vals * 2.0 ** s - x)
+                best = np.flatnonzero(err == err.min())
+                if len(best) > 1:                     # tie: the even code (sign agrees with x)
+                    best = [c for c in best if finite[c] % 2 == 0 and (np.signbit(x) == (finite[c] >= 0x80))]
+                codes[idx + (32 * b + t,)] = finite[best[0]]
+    return codes, scales
+
+
+def test_mx_quantize_matches_brute_force():
+    g = np.random.default_rng(2)
+    v = g.normal(0, 1, (3, 64)) * np.exp2(g.integers(-6, 6, (3, 1)))
+    v[1, 32:] = 0.0                                     # an all-zero block
+    v[2, :32] *= 1e-30                                  # tiny values: scale exponent far below 0
+    codes, scales = oracle.mx_quantize(v, axis=1)
+    bc, bs = _brute_force_quantize(v)
+    np.testing.assert_array_equal(scales, bs)
+    # +0 / -0 may differ for elements that round to zero; compare values then
+    np.testing.assert_array_equal(oracle.e4m3_to_f64(codes), oracle.e4m3_to_f64(bc))
+
+
+def test_mx_quantize_axis0_equals_transposed_axis1():
+    g = np.random.default_rng(3)
+    v = g.normal(0, 1, (64, 48))
+    c0, s0 = oracle.mx_quantize(v, axis=0)
+    c1, s1 = oracle.mx_quantize(v.T, axis=1)
+    np.testing.assert_array_equal(c0, c1.T)
+    np.testing.assert_array_equal(s0, s1.T)
+
+
+def test_mx_roundtrip_of_representable_values_and_error_bound():
+    g = np.random.default_rng(4)
+    codes = g.integers(0, 0x7F, (4, 96)).astype(np.uint8) | (g.integers(0, 2, (4, 96)) * 0x80).astype(np.uint8)
+    codes[:, ::32] = 0x7E                               # every block holds +-448 once: exponent = s
+    s = g.integers(-20, 20, (4, 3)).astype(np.int64)
+    v = oracle.mx_dequantize(codes, (s + 127).astype(np.uint8), axis=1)
+    c2, s2 = oracle.mx_quantize(v, axis=1)
+    np.testing.assert_array_equal(s2.astype(np.int64) - 127, s)
+    np.testing.assert_array_equal(oracle.e4m3_to_f64(c2), oracle.e4m3_to_f64(codes))
+    # arbitrary data: relative error of a normal-range element is at most 2^-4 (3 mantissa bits)
+    w = g.normal(0, 1, (8, 256))
+    cw, sw = oracle.mx_quantize(w, axis=1)
+    back = oracle.mx_dequantize(cw, sw, axis=1)
+    big = np.abs(w) >= np.repeat(oracle.e8m0_to_f64(sw), 32, axis=1) * 2.0 ** -6
+    assert np.all(np.abs(back - w)[big] <= np.abs(w)[big] * 2.0 ** -4)
