@@ -15,6 +15,7 @@ Helpers that read rocprofv3 CSV output (CPU only, print a text summary):
 
     python bench.py --summarize-stats DIR --config C --command "..."
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR --config C --command "..."
+    python bench.py --summarize-mfma DIR --config C --command "..."
 """
 from __future__ import annotations
 
@@ -52,7 +53,7 @@ STAGE_KERNEL_BF16 = {"gemm_up": "moe::grouped_gemm_kernel<0,", "gemm_down": "moe
                      "combine": "moe::combine_kernel", "router": "moe::router_topk_kernel",
                      "dlogits": "moe::dlogits_kernel", "wg_reduce": "moe::wg_reduce_kernel",
                      "plan": "moe::plan_", "tile_map": "moe::tile_map_kernel", "wg_split": "moe::wg_split_kernel",
-                     "tokrow": "moe::tokrow_kernel"}
+                     "tokrow": "moe::tokrow_kernel", "permute": "moe::permute_kernel"}
 STAGE_KERNEL_FP8 = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_fp8_kernel<0>",
                         gemm_down="moe::grouped_gemm_fp8_kernel<1>", gemm_dact="moe::grouped_gemm_fp8_kernel<2>",
                         gemm_dx="moe::grouped_gemm_fp8_kernel<3>", quant_dy="moe::quant_rows_kernel",
@@ -94,10 +95,13 @@ def stage_bytes(stage, T, d, f, E, k, A):
     return None
 
 
-def kernel_source_hash():
+SOURCE_DIR = os.path.join(ROOT, "grouped_gemm_expert_router_amd", "csrc")
+
+
+def kernel_source_hash(src_dir=None):
     """Hash of every kernel and ABI source; a stored counter summary is only used while it matches."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "grouped_gemm_expert_router_amd", "csrc", "*"))):
+    for p in sorted(glob.glob(os.path.join(src_dir or SOURCE_DIR, "*"))):
         with open(p, "rb") as fh:
             h.update(os.path.basename(p).encode())
             h.update(fh.read())
@@ -212,7 +216,7 @@ def summarize_stats(d, config, command):
     rows = _csv_rows(d, "kernel_stats.csv")
     print(f"# rocprofv3 kernel statistics: {WORKLOADS[config]}")
     print(f"command: {command}")
-    print(f"source_hash: {kernel_source_hash()}")
+    print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
     print(f"{'stage':<12} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}  kernel")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         st = _stage_of(r["Name"], config) or "-"
@@ -244,7 +248,7 @@ def summarize_counters(fetch_dir, write_dir, config, command):
     ff, fw = calib(fetch, "FETCH_SIZE"), calib(write, "WRITE_SIZE")
     print(f"# rocprofv3 HBM byte counters per dispatch: {WORKLOADS[config]}")
     print(f"command: {command}")
-    print(f"source_hash: {kernel_source_hash()}")
+    print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
     print(f"calibration: torch.neg over {CALIB_MIB} MiB fp32 -> fetch_factor={ff:.4f} write_factor={fw:.4f}")
     print("# stage <name> kernel=<symbol> fetch_kib=<median raw> write_kib=<median raw> traffic_bytes=<scaled sum>")
     for name in sorted(set(fetch) & set(write)):
@@ -256,6 +260,29 @@ def summarize_counters(fetch_dir, write_dir, config, command):
         tb = fk * 1024.0 * ff + wk * 1024.0 * fw
         print(f"stage {st} fetch_kib={fk:.1f} write_kib={wk:.1f} traffic_bytes={tb:.0f} "
               f"kernel={name.split('(')[0].replace(' ', '')}")
+
+
+def summarize_mfma(d, config, command):
+    """MFMA pipe utilisation per kernel: SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs)
+    over 1024 x the kernel's cycles per XCD (GRBM_GUI_ACTIVE is summed over the 8 XCDs)."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    print(f"# rocprofv3 MFMA utilisation per dispatch: {WORKLOADS[config]}")
+    print(f"command: {command}")
+    print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
+    print("# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); medians over dispatches")
+    print(f"{'stage':<12} {'mfma_busy':>9} {'mfma_insts':>12} {'lds_bank_conf/cu_cyc':>21}  kernel")
+    med = lambda v: sorted(v)[len(v) // 2]
+    for name, c in sorted(acc.items()):
+        st = _stage_of(name, config)
+        if st is None or not st.startswith("gemm") or "SQ_VALU_MFMA_BUSY_CYCLES" not in c:
+            continue
+        cyc = med(c["GRBM_GUI_ACTIVE"]) / 8.0
+        busy = med(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / (1024.0 * cyc)
+        bc = med(c["SQ_LDS_BANK_CONFLICT"]) / (256.0 * cyc) if "SQ_LDS_BANK_CONFLICT" in c else float("nan")
+        ins = med(c["SQ_INSTS_MFMA"]) if "SQ_INSTS_MFMA" in c else float("nan")
+        print(f"{st:<12} {busy:>9.3f} {ins:>12.4g} {bc:>21.4f}  {name.split('(')[0].replace('void ', '')}")
 
 
 # ------------------------------------------------------------------ benchmark
@@ -271,12 +298,19 @@ def main():
                     help=f"run a {CALIB_MIB} MiB copy kernel first (calibrates profiler byte counters)")
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-mfma", metavar="DIR")
     ap.add_argument("--command", default="", help="profiler command recorded in a summary")
+    ap.add_argument("--source-dir", default=None, help="kernel sources the profiled run used (for the hash)")
     args = ap.parse_args()
+    global SOURCE_DIR
+    if args.source_dir:
+        SOURCE_DIR = args.source_dir
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats, args.config, args.command)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters, args.config, args.command)
+    if args.summarize_mfma:
+        return summarize_mfma(args.summarize_mfma, args.config, args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this layer is one GPU's share of an expert-parallel "
               f"layer and the build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -291,7 +325,8 @@ def main():
     moe.load_library()
     t_gen = time.perf_counter()
     inp = make_config(args.config)
-    log(f"[bench] generated {args.config} inputs in {time.perf_counter() - t_gen:.1f}s")
+    log(f"[bench] generated {args.config} inputs in {time.perf_counter() - t_gen:.1f}s; kernel sources "
+        f"{kernel_source_hash()}")
     fp8 = inp.dtype == "fp8"
     T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
     dm = moe.dims(T, d, f, E, k, moe.MOE_FP8_E4M3 if fp8 else moe.MOE_BF16)
@@ -343,18 +378,21 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    # HIP events on the launch stream around every kernel of the timed steps
+    # HIP events on the launch stream around every kernel of the timed steps (the backward runs
+    # its weight-gradient chain on the library's second stream)
     cur = torch.cuda.current_stream()
-    events, open_ev = [], {}
+    events, open_ev, streams = [], {}, {}
 
     def hook(stage, begin, stream_ptr):
-        assert (stream_ptr or 0) == (cur.cuda_stream or 0), "kernel launched on another stream"
+        sp = stream_ptr or 0
+        if sp not in streams:
+            streams[sp] = cur if sp == (cur.cuda_stream or 0) else torch.cuda.ExternalStream(sp)
         ev = torch.cuda.Event(enable_timing=True)
-        ev.record(cur)
+        ev.record(streams[sp])
         if begin:
-            open_ev[stage] = ev
+            open_ev[(stage, sp)] = ev
         else:
-            events.append((stage, open_ev.pop(stage), ev))
+            events.append((stage, open_ev.pop((stage, sp)), ev))
 
     moe.moe_set_stage_hook(hook)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -409,6 +447,24 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": by,
                 "avg_launch_ms": dom_e["avg_ms"]}
 
+    # dispatch on its own (the step fuses it into the first GEMM's loads): HBM bandwidth of the
+    # standalone permute kernel, outside the timed region
+    permute = None
+    if not fp8:
+        xp = torch.empty((T * k, d), dtype=torch.bfloat16, device=dev)
+        moe.moe_permute(dm, x, b["perm"], b["offsets"], xp)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(cur)
+        for _ in range(10):
+            moe.moe_permute(dm, x, b["perm"], b["offsets"], xp)
+        p1.record(cur)
+        torch.cuda.synchronize()
+        pms = p0.elapsed_time(p1) / 10
+        pby = T * d * 2 + A * d * 2
+        permute = {"avg_ms": pms, "algorithmic_bytes": pby, "gbs": pby / (pms * 1e-3) / 1e9,
+                   "frac_hbm_peak": pby / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del xp
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f}s sample) ...")
@@ -424,7 +480,8 @@ def main():
         "tokens_per_s": T / (ms * 1e-3),
         "frac_of_bf16_peak": tflops / PEAK_TFLOPS["bf16"],
         "frac_of_mfma_peak": ideal_ms / ms,
-        "useful_flop_per_step": useful, "stages": stages, "roofline": roof, "cpu_baseline": cpu,
+        "useful_flop_per_step": useful, "stages": stages, "permute_standalone": permute, "roofline": roof,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
