@@ -61,12 +61,23 @@ STAGE_KERNEL_FP8 = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_fp8_kernel
 FP8_STAGES = ("gemm_up", "gemm_down", "gemm_dact", "gemm_dx")
 
 
+def workload_name(run_name):
+    base, _, dt = run_name.partition(":")
+    return WORKLOADS[base] + (", run as MXFP8 (quantised per call)" if dt == "mxfp8" else "")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+STAGE_KERNEL_MX = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_mx_kernel<0>",
+                       gemm_down="moe::grouped_gemm_mx_kernel<1>", gemm_dact="moe::grouped_gemm_mx_kernel<2>",
+                       gemm_dx="moe::grouped_gemm_mx_kernel<3>", mx_quant="moe::mx_quant_")
+
+
 def is_fp8(config):
-    return config.endswith("fp8")
+    """True for the fp8 runs: the blockwise-fp8 workload or any workload run as MXFP8."""
+    return config.endswith("fp8") or config.endswith(":mxfp8")
 
 
 def stage_dtype(config, stage):
@@ -74,6 +85,8 @@ def stage_dtype(config, stage):
 
 
 def stage_kernels(config):
+    if config.endswith(":mxfp8"):
+        return STAGE_KERNEL_MX
     return STAGE_KERNEL_FP8 if is_fp8(config) else STAGE_KERNEL_BF16
 
 
@@ -92,6 +105,10 @@ def stage_bytes(stage, T, d, f, E, k, A):
         return T * d * 2 + T * d + T * (d // 128) * 4
     if stage == "dequant_x":
         return T * d + T * (d // 128) * 4 + T * d * 2
+    if stage in ("mx_quant_x", "mx_quant_dy"):
+        return T * d * 2 + T * d + T * d // 32
+    if stage in ("mx_quant_w1", "mx_quant_w2"):
+        return E * d * f * (2 + 1) + E * d * f // 32     # one of W1 (2df) / W2 (df): bytes of W1 halved
     return None
 
 
@@ -109,7 +126,7 @@ def kernel_source_hash(src_dir=None):
 
 
 def traffic_file(config):
-    return os.path.join(ROOT, "profiles", f"hbm_traffic_{config}.txt")
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{config.replace(':', '_')}.txt")
 
 
 def stored_traffic(config, stage):
@@ -214,7 +231,7 @@ def _stage_of(name, config):
 
 def summarize_stats(d, config, command):
     rows = _csv_rows(d, "kernel_stats.csv")
-    print(f"# rocprofv3 kernel statistics: {WORKLOADS[config]}")
+    print(f"# rocprofv3 kernel statistics: {workload_name(config)}")
     print(f"command: {command}")
     print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
     print(f"{'stage':<12} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}  kernel")
@@ -246,7 +263,7 @@ def summarize_counters(fetch_dir, write_dir, config, command):
         v = sorted(acc[ks[0]])[len(acc[ks[0]]) // 2] * 1024.0
         return copy_bytes / v
     ff, fw = calib(fetch, "FETCH_SIZE"), calib(write, "WRITE_SIZE")
-    print(f"# rocprofv3 HBM byte counters per dispatch: {WORKLOADS[config]}")
+    print(f"# rocprofv3 HBM byte counters per dispatch: {workload_name(config)}")
     print(f"command: {command}")
     print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
     print(f"calibration: torch.neg over {CALIB_MIB} MiB fp32 -> fetch_factor={ff:.4f} write_factor={fw:.4f}")
@@ -268,7 +285,7 @@ def summarize_mfma(d, config, command):
     acc = {}
     for r in _csv_rows(d, "counter_collection.csv"):
         acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    print(f"# rocprofv3 MFMA utilisation per dispatch: {WORKLOADS[config]}")
+    print(f"# rocprofv3 MFMA utilisation per dispatch: {workload_name(config)}")
     print(f"command: {command}")
     print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
     print("# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); medians over dispatches")
@@ -292,6 +309,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="qwen3", choices=sorted(WORKLOADS))
+    ap.add_argument("--dtype", default="auto", choices=["auto", "mxfp8"],
+                    help="auto: the workload's own format; mxfp8: run a bf16 workload as MXFP8 (quantised inside)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -305,12 +324,13 @@ def main():
     global SOURCE_DIR
     if args.source_dir:
         SOURCE_DIR = args.source_dir
+    run_name = args.config + (":mxfp8" if args.dtype == "mxfp8" else "")
     if args.summarize_stats:
-        return summarize_stats(args.summarize_stats, args.config, args.command)
+        return summarize_stats(args.summarize_stats, run_name, args.command)
     if args.summarize_counters:
-        return summarize_counters(*args.summarize_counters, args.config, args.command)
+        return summarize_counters(*args.summarize_counters, run_name, args.command)
     if args.summarize_mfma:
-        return summarize_mfma(args.summarize_mfma, args.config, args.command)
+        return summarize_mfma(args.summarize_mfma, run_name, args.command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this layer is one GPU's share of an expert-parallel "
               f"layer and the build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -328,8 +348,10 @@ def main():
     log(f"[bench] generated {args.config} inputs in {time.perf_counter() - t_gen:.1f}s; kernel sources "
         f"{kernel_source_hash()}")
     fp8 = inp.dtype == "fp8"
+    mx = args.dtype == "mxfp8"
+    assert not (mx and fp8), "the blockwise-fp8 workload has its own format"
     T, d, f, E, k = inp.T, inp.d, inp.f, inp.E, inp.k
-    dm = moe.dims(T, d, f, E, k, moe.MOE_FP8_E4M3 if fp8 else moe.MOE_BF16)
+    dm = moe.dims(T, d, f, E, k, moe.MOE_FP8_E4M3 if fp8 else (moe.MOE_MXFP8 if mx else moe.MOE_BF16))
     dev = "cuda"
 
     def bf16(a):
@@ -419,8 +441,8 @@ def main():
         ent = {"launches": len(ts), "avg_ms": avg, "ms_per_step": sum(ts) / args.steps}
         if stage in GEMM_FLOP_PER_PAIR:
             fl = GEMM_FLOP_PER_PAIR[stage] * A * d * f
-            pk = PEAK_TFLOPS[stage_dtype(args.config, stage)]
-            ent.update(dtype=stage_dtype(args.config, stage), tflops=fl / (avg * 1e-3) / 1e12)
+            pk = PEAK_TFLOPS[stage_dtype(run_name, stage)]
+            ent.update(dtype=stage_dtype(run_name, stage), tflops=fl / (avg * 1e-3) / 1e12)
             ent["frac_mfma_peak"] = ent["tflops"] / pk
             ideal_ms += fl / (pk * 1e12) * 1e3
         else:
@@ -432,13 +454,13 @@ def main():
                                            sorted(stages.items(), key=lambda kv: -kv[1]["ms_per_step"])))
     dom = max(stages, key=lambda s: stages[s]["ms_per_step"])
     dom_e = stages[dom]
-    traffic = stored_traffic(args.config, dom)
+    traffic = stored_traffic(run_name, dom)
     if dom in GEMM_FLOP_PER_PAIR:
         fl = GEMM_FLOP_PER_PAIR[dom] * A * d * f
-        pk = PEAK_TFLOPS[stage_dtype(args.config, dom)]
+        pk = PEAK_TFLOPS[stage_dtype(run_name, dom)]
         achieved = fl / (dom_e["avg_ms"] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": pk, "unit": "TFLOP/s",
-                "frac": achieved / pk, "traffic": traffic, "dtype": stage_dtype(args.config, dom),
+                "frac": achieved / pk, "traffic": traffic, "dtype": stage_dtype(run_name, dom),
                 "algorithmic_flop_per_launch": fl, "avg_launch_ms": dom_e["avg_ms"]}
     else:
         by = stage_bytes(dom, T, d, f, E, k, A)
@@ -452,11 +474,12 @@ def main():
     permute = None
     if not fp8:
         xp = torch.empty((T * k, d), dtype=torch.bfloat16, device=dev)
-        moe.moe_permute(dm, x, b["perm"], b["offsets"], xp)
+        pdm = moe.dims(T, d, f, E, k)  # the permute moves bf16 rows
+        moe.moe_permute(pdm, x, b["perm"], b["offsets"], xp)
         p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         p0.record(cur)
         for _ in range(10):
-            moe.moe_permute(dm, x, b["perm"], b["offsets"], xp)
+            moe.moe_permute(pdm, x, b["perm"], b["offsets"], xp)
         p1.record(cur)
         torch.cuda.synchronize()
         pms = p0.elapsed_time(p1) / 10
@@ -474,9 +497,10 @@ def main():
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8_e4m3+bf16" if fp8 else "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "T": T, "d": d, "f": f, "E": E, "k": k,
-                   "routed_pairs": A, "seed_config": args.config},
+        "vs_baseline": None, "dtype": "fp8_e4m3+bf16" if fp8 else ("mxfp8+bf16" if mx else "bf16"),
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config] + (", run as MXFP8 (quantised per call)" if mx else ""),
+                   "T": T, "d": d, "f": f, "E": E, "k": k, "routed_pairs": A, "seed_config": run_name},
         "tokens_per_s": T / (ms * 1e-3),
         "frac_of_bf16_peak": tflops / PEAK_TFLOPS["bf16"],
         "frac_of_mfma_peak": ideal_ms / ms,

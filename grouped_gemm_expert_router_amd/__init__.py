@@ -13,12 +13,12 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_BF16, MOE_FP8_E4M3 = 0, 1
+MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = 0, 1, 2
 MOE_WS_ROUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD = 0, 1, 2
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
 
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_saved_bytes", "moe_route", "moe_plan", "moe_forward", "moe_backward",
-                "moe_permute", "moe_combine", "moe_set_stage_hook", "moe_status_string")
+                "moe_permute", "moe_combine", "moe_mxfp8_quantize", "moe_set_stage_hook", "moe_status_string")
 
 
 class MoeDims(ctypes.Structure):
@@ -61,6 +61,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_backward.argtypes = [dp] + [vp] * 19 + [sz, vp]
     lib.moe_permute.argtypes = [dp, vp, vp, vp, vp, vp]
     lib.moe_combine.argtypes = [dp, vp, vp, vp, vp]
+    lib.moe_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, i32, vp, vp, vp]
     lib.moe_set_stage_hook.argtypes = [STAGE_HOOK, vp]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -154,6 +155,11 @@ def moe_combine(dm, op, inv_perm, y, stream=None):
                                                      _stream(stream)))
 
 
+def moe_mxfp8_quantize(src, batch, rows, cols, block_axis, codes, exps, stream=None):
+    _check("moe_mxfp8_quantize", load_library().moe_mxfp8_quantize(_ptr(src), batch, rows, cols, block_axis,
+                                                                   _ptr(codes), _ptr(exps), _stream(stream)))
+
+
 _hook_ref = None
 
 
@@ -207,6 +213,7 @@ def alloc_layer_buffers(dm: MoeDims, device="cuda", backward: bool = True) -> di
 
 __all__ = ["MoeDims", "MoEError", "dims", "load_library", "status_string", "moe_workspace_bytes", "moe_saved_bytes",
            "moe_route", "moe_plan", "moe_forward", "moe_backward", "moe_permute", "moe_combine",
-           "moe_set_stage_hook", "alloc_layer_buffers", "ENTRY_POINTS", "MOE_BF16", "MOE_FP8_E4M3", "MOE_WS_ROUTE", "MOE_WS_FORWARD",
+           "moe_mxfp8_quantize", "moe_set_stage_hook", "alloc_layer_buffers", "ENTRY_POINTS", "MOE_BF16",
+           "MOE_FP8_E4M3", "MOE_MXFP8", "MOE_WS_ROUTE", "MOE_WS_FORWARD",
            "MOE_WS_BACKWARD", "MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_ERR_ALIGN"]

@@ -24,32 +24,38 @@ int check_dims(const moe_dims* d) {
   if (d->T < 0 || d->E < 1 || d->E > 1024 || d->k < 1 || d->k > d->E || d->k > 64) return MOE_ERR_SHAPE;
   if (d->d <= 0 || d->f <= 0 || d->d % 128 || d->f % 128 || d->d > 65536 || d->f > 65536) return MOE_ERR_SHAPE;
   if (d->T * d->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
-  if (d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3) return MOE_ERR_DTYPE;
-  // the fp8 tiles are 256 columns wide along both d and f
-  if (d->dtype == MOE_FP8_E4M3 && (d->d % 256 || d->f % 256)) return MOE_ERR_SHAPE;
+  if (d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3 && d->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  // the fp8 and MXFP8 tiles are 256 columns wide along both d and f
+  if (d->dtype != MOE_BF16 && (d->d % 256 || d->f % 256)) return MOE_ERR_SHAPE;
   // launch grids of the ragged GEMMs must fit in 32 bits
   const int64_t A = d->T * d->k;
-  const int bm = d->dtype == MOE_FP8_E4M3 ? kFp8BM : kGemmBM;
+  const int bm = d->dtype != MOE_BF16 ? kFp8BM : kGemmBM;
   const int64_t rows = (A + bm - 1) / bm + (A < d->E ? A : d->E);
   if (rows * (d->f / 64 > d->d / 128 ? d->f / 64 : d->d / 128) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
 bool is_fp8(const moe_dims* d) { return d->dtype == MOE_FP8_E4M3; }
-int row_tile(const moe_dims* d) { return is_fp8(d) ? kFp8BM : kGemmBM; }
+bool is_mx(const moe_dims* d) { return d->dtype == MOE_MXFP8; }
+int row_tile(const moe_dims* d) { return d->dtype != MOE_BF16 ? kFp8BM : kGemmBM; }
 // d_topk_w partial sums per routed pair written by the activation-gradient GEMM
-int dact_parts(const moe_dims* d) { return is_fp8(d) ? (int)d->f / 256 : (int)d->f / dact_bn((int)d->f); }
+int dact_parts(const moe_dims* d) {
+  return d->dtype != MOE_BF16 ? (int)d->f / 256 : (int)d->f / dact_bn((int)d->f);
+}
 
 MoeShape shape_of(const moe_dims* d) {
   return MoeShape{(int)d->T, (int)d->d, (int)d->f, (int)d->E, (int)d->k};
 }
 
-// fp8 only: asq/ass (As in e4m3 + scales); dyq/dys, dHq/dHs, xb (x dequantised to bf16).
+// fp8: asq/ass (As in e4m3 + scales); dyq/dys, dHq/dHs, xb (x dequantised to bf16).
+// MXFP8 (codes + E8M0 exponents): asq/ass; xq/xe, w1q/w1e and w2q/w2e (forward quantisation of
+// x, W1 and W2); dyq/dys, dHq/dHs, w1q/w1e and w2q/w2e (W1, W2 along the data gradients' K).
 struct FwdLayout {
-  size_t tiles, ntiles, op, asq, ass, total;
+  size_t tiles, ntiles, op, asq, ass, xq, xe, w1q, w1e, w2q, w2e, total;
 };
 struct BwdLayout {
-  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dHq, dHs, xb, total;
+  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dHq, dHs, xb, w1q,
+      w1e, w2q, w2e, total;
   int max_partials;
 };
 struct SavedLayout {
@@ -71,6 +77,25 @@ FwdLayout fwd_layout(const moe_dims* d) {
     off += al256((size_t)A * d->f);
     L.ass = off;
     off += al256((size_t)A * (d->f / 128) * sizeof(float));
+  }
+  if (is_mx(d)) {
+    const size_t E = d->E, dd = d->d, ff = d->f, T = d->T;
+    L.asq = off;
+    off += al256((size_t)A * ff);
+    L.ass = off;
+    off += al256((size_t)A * (ff / 32));
+    L.xq = off;
+    off += al256(T * dd);
+    L.xe = off;
+    off += al256(T * (dd / 32));
+    L.w1q = off;
+    off += al256(E * dd * 2 * ff);
+    L.w1e = off;
+    off += al256(E * dd * 2 * ff / 32);
+    L.w2q = off;
+    off += al256(E * ff * dd);
+    L.w2e = off;
+    off += al256(E * ff * dd / 32);
   }
   L.total = off;
   return L;
@@ -112,6 +137,25 @@ BwdLayout bwd_layout(const moe_dims* d) {
     off += al256((size_t)A * (2 * d->f / 128) * sizeof(float));
     L.xb = off;
     off += al256((size_t)d->T * d->d * 2);
+  }
+  if (is_mx(d)) {
+    const size_t E = d->E, dd = d->d, ff = d->f, T = d->T;
+    L.dyq = off;
+    off += al256(T * dd);
+    L.dys = off;
+    off += al256(T * (dd / 32));
+    L.dHq = off;
+    off += al256((size_t)A * 2 * ff);
+    L.dHs = off;
+    off += al256((size_t)A * (2 * ff / 32));
+    L.w1q = off;
+    off += al256(E * dd * 2 * ff);
+    L.w1e = off;
+    off += al256(E * dd * 2 * ff / 32);
+    L.w2q = off;
+    off += al256(E * ff * dd);
+    L.w2e = off;
+    off += al256(E * ff * dd / 32);
   }
   L.total = off;
   return L;
@@ -241,6 +285,20 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
   uint16_t* H = (uint16_t*)(sv + SL.H);
   uint16_t* As = (uint16_t*)(sv + SL.As);
   hipStream_t st = (hipStream_t)stream;
+  if (is_mx(dims)) {
+    uint8_t *Asq = (uint8_t*)(w + L.asq), *Ase = (uint8_t*)(w + L.ass);
+    uint8_t *xq = (uint8_t*)(w + L.xq), *xe = (uint8_t*)(w + L.xe);
+    uint8_t *w1q = (uint8_t*)(w + L.w1q), *w1e = (uint8_t*)(w + L.w1e);
+    uint8_t *w2q = (uint8_t*)(w + L.w2q), *w2e = (uint8_t*)(w + L.w2e);
+    MOE_TRY("mx_quant_x", launch_mx_quant((const uint16_t*)x, 1, s.T, s.d, 0, xq, xe, st));
+    MOE_TRY("mx_quant_w1", launch_mx_quant((const uint16_t*)W1, s.E, s.d, 2 * s.f, 1, w1q, w1e, st));
+    MOE_TRY("mx_quant_w2", launch_mx_quant((const uint16_t*)W2, s.E, s.f, s.d, 1, w2q, w2e, st));
+    MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
+    MOE_TRY("gemm_up", launch_mx_up(s, xq, xe, w1q, w1e, topk_w, offsets, perm, tiles, ntiles, H, As, Asq, Ase, st));
+    MOE_TRY("gemm_down", launch_mx_down(s, Asq, Ase, w2q, w2e, offsets, perm, tiles, ntiles, Op, st));
+    MOE_TRY("combine", launch_combine(Op, inv_perm, s.T, s.d, s.k, (uint16_t*)y, st));
+    return MOE_OK;
+  }
   if (fp8) {
     uint8_t* Asq = (uint8_t*)(w + L.asq);
     float* Ass = (float*)(w + L.ass);
@@ -308,6 +366,29 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   const uint16_t* As = (const uint16_t*)(sv + SL.As);
   hipStream_t st = (hipStream_t)stream;
   const WgSplit sp = wg_split_of(L, w, offsets);
+  if (is_mx(dims)) {
+    uint8_t *dyq = (uint8_t*)(w + L.dyq), *dye = (uint8_t*)(w + L.dys);
+    uint8_t *dHq = (uint8_t*)(w + L.dHq), *dHe = (uint8_t*)(w + L.dHs);
+    uint8_t *w1q = (uint8_t*)(w + L.w1q), *w1e = (uint8_t*)(w + L.w1e);
+    uint8_t *w2q = (uint8_t*)(w + L.w2q), *w2e = (uint8_t*)(w + L.w2e);
+    MOE_TRY("mx_quant_dy", launch_mx_quant((const uint16_t*)dy, 1, s.T, s.d, 0, dyq, dye, st));
+    MOE_TRY("mx_quant_w2", launch_mx_quant((const uint16_t*)W2, 1, s.E * s.f, s.d, 0, w2q, w2e, st));
+    MOE_TRY("mx_quant_w1", launch_mx_quant((const uint16_t*)W1, 1, s.E * s.d, 2 * s.f, 0, w1q, w1e, st));
+    MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
+    MOE_TRY("gemm_dact", launch_mx_dact(s, dyq, dye, w2q, w2e, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq, dHe,
+                                        dwp, st));
+    MOE_TRY("gemm_dx", launch_mx_dx(s, dHq, dHe, w1q, w1e, offsets, perm, tiles, ntiles, dXp, st));
+    MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
+    MOE_TRY("tokrow", launch_tokrow(perm, offsets, s.E, (int64_t)s.T * s.k, s.k, tokrow, st));
+    MOE_TRY("wg_split", launch_wg_split(s, offsets, sp, st));
+    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, sp, (uint16_t*)dW2, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.f * s.d, (uint16_t*)dW2, st));
+    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, tokrow, sp, (uint16_t*)dW1, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.d * 2 * s.f, (uint16_t*)dW1, st));
+    MOE_TRY("dlogits", launch_dlogits(dwp, dact_parts(dims), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w,
+                                      d_logits, st));
+    return MOE_OK;
+  }
   if (fp8) {
     uint8_t* dyq = (uint8_t*)(w + L.dyq);
     float* dys = (float*)(w + L.dys);
@@ -373,6 +454,20 @@ int moe_combine(const moe_dims* dims, const void* op, const int32_t* inv_perm, v
   MOE_TRY("combine", launch_combine((const uint16_t*)op, inv_perm, (int)dims->T, (int)dims->d, (int)dims->k,
                                    (uint16_t*)y, st));
 
+  return MOE_OK;
+}
+
+int moe_mxfp8_quantize(const void* src, int64_t batch, int64_t rows, int64_t cols, int block_axis, void* codes,
+                       void* exps, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || (block_axis != 0 && block_axis != 1)) return MOE_ERR_SHAPE;
+  if (rows > (1 << 30) || cols > (1 << 30) || batch * rows * cols >= ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  if (block_axis == 1 ? (cols % 32 != 0) : (rows % 32 != 0 || cols % 8 != 0)) return MOE_ERR_SHAPE;
+  if (batch * rows * cols == 0) return MOE_OK;
+  if (!src || !codes || !exps) return MOE_ERR_NULL;
+  if (!al16(src) || !al16(codes) || ((uintptr_t)exps & 7u)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("mx_quant", launch_mx_quant((const uint16_t*)src, batch, (int)rows, (int)cols, block_axis == 0 ? 1 : 0,
+                                      (uint8_t*)codes, (uint8_t*)exps, st));
   return MOE_OK;
 }
 

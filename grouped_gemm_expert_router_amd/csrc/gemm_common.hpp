@@ -116,4 +116,79 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_byte_addr) {
                : "memory", "m0");
 }
 
+// ---------------------------------------------------------------- fp8 (OCP e4m3) operand tiles
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// KN fp8 layout: [k][256 bytes]; chunk c (16 columns) of k row r lives at chunk c ^ (2 * (r & 7)).
+__device__ __forceinline__ uint32_t kn8_off(int kr, int col) {
+  return kr * 256 + ((((col >> 4) ^ (2 * (kr & 7)))) << 4) + (col & 15);
+}
+
+// 32-column fragment at column cbase, 64-deep step kk: lane holds column cbase + lane%32 and
+// k = 64*kk + 32*(lane/32) + 0..31.  Within a 16-lane group, lane s supplies the address of
+// (k = k0 + s/2, col = c0 + 8*(s%2)) and lane i receives the 8 bytes (k0..k0+7, c0 + i).
+__device__ __forceinline__ i32x8 read_kn8(uint32_t base, int cbase, int kk, int lane) {
+  const int grp = lane >> 4, i16 = lane & 15;
+  const int col = cbase + 16 * (grp & 1) + 8 * (i16 & 1);
+  const int krb = 64 * kk + 32 * (grp >> 1) + (i16 >> 1);
+  i32x8 v;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const i32x2v t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2v*)(uintptr_t)(base + kn8_off(krb + 8 * h, col)));
+    v[2 * h] = t.x;
+    v[2 * h + 1] = t.y;
+  }
+  return v;
+}
+
+// KM fp8 layout: [row][128 bytes], chunk c of row r at chunk c ^ ((r >> 1) & 7); 32 bytes per
+// lane = two chunks.
+__device__ __forceinline__ i32x8 read_km8(uint32_t base, int row, int kk, int lane) {
+  const int c = 4 * kk + 2 * (lane >> 5);
+  const u32x4 lo = *(const LDS_AS u32x4*)(uintptr_t)(base + km_off<64>(row, c));
+  const u32x4 hi = *(const LDS_AS u32x4*)(uintptr_t)(base + km_off<64>(row, c + 1));
+  i32x8 v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// The same fragments in the k order the block-scaled MFMA assigns to its two 32-value scale
+// blocks: bytes 0..15 of lane l hold k = 64*kk + 16*(l/32) + 0..15 and bytes 16..31 hold
+// k = 64*kk + 32 + 16*(l/32) + 0..15, so scale block b of the step (lane l's exponent for
+// b = l/32) covers k = 64*kk + 32*b + 0..31.  (An unscaled product only needs A and B in the same
+// order; per-block exponents need this one.)
+__device__ __forceinline__ i32x8 read_kn8_mx(uint32_t base, int cbase, int kk, int lane) {
+  const int grp = lane >> 4, i16 = lane & 15, half = grp >> 1;
+  const int col = cbase + 16 * (grp & 1) + 8 * (i16 & 1);
+  i32x8 v;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int k0 = 64 * kk + (h < 2 ? 16 * half + 8 * h : 32 + 16 * half + 8 * (h - 2));
+    const i32x2v t =
+        __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2v*)(uintptr_t)(base + kn8_off(k0 + (i16 >> 1), col)));
+    v[2 * h] = t.x;
+    v[2 * h + 1] = t.y;
+  }
+  return v;
+}
+__device__ __forceinline__ i32x8 read_km8_mx(uint32_t base, int row, int kk, int lane) {
+  const int half = lane >> 5;
+  const u32x4 lo = *(const LDS_AS u32x4*)(uintptr_t)(base + km_off<64>(row, 4 * kk + half));
+  const u32x4 hi = *(const LDS_AS u32x4*)(uintptr_t)(base + km_off<64>(row, 4 * kk + 2 + half));
+  i32x8 v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// e4m3 with round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  auto sat = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
+}
+
 }  // namespace moe

@@ -1,0 +1,580 @@
+// MXFP8 ragged grouped GEMMs and quantisers for gfx950.  MXFP8 (named on the JAX MoE page,
+// "Az NVIDIA szerint tízszer gyorsabb lett a dropless MoE tanítása JAX-ban", section
+// "Csoportosított mátrixszorzás és összevont adatmozgatás", and on the TE MoE page,
+// "NVIDIA מציגה דרך יעילה לאמן מודלי MoE בביולוגיה", section "צמצום הזיכרון ותקורות הכימות")
+// shares one power-of-two scale per 32 consecutive values.  Here the blocks run along each
+// GEMM's K, so the E8M0 exponents go straight into the per-lane scale operands of
+// v_mfma_scale_f32_32x32x64_f8f6f4: in a 32x32x64 step lane l gives the exponent of row
+// (column) l % 32 for k block l / 32 of the step, and its 32 operand bytes are two 16-byte
+// halves, one from each block (read_k*8_mx).  No software promotion is needed.
+//
+// Inputs stay 16-bit (the master weights): the quantisers below produce, per call, x and dy in
+// row blocks (K = d), W1 and W2 in column blocks for the forward (K = d and f) and in row blocks
+// for the data gradients (K = 2f and d).  The epilogues requantise As (K = f of the down
+// projection) and dH (K = 2f of dX) the same way.  The block exponent is the smallest power of
+// two that brings the block's maximum magnitude within 448, so no element is clipped.
+//
+// Tiles are 256 x 256 x 128 (four scale blocks per stage) with 8 waves (2 x 4) of 128 x 64.
+#include "common.hpp"
+#include "gemm_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+enum MxMode { X_UP = 0, X_DOWN = 1, X_DACT = 2, X_DX = 3 };
+
+#ifndef MX_GM
+#define MX_GM 8
+#endif
+
+struct MxArgs {
+  const uint8_t* A;   // e4m3 rows, K contiguous
+  int64_t lda;        // bytes
+  const uint8_t* Ae;  // E8M0 [rows, K/32]
+  int64_t lde_a;
+  const uint8_t* B;   // e4m3 weights of all experts
+  int64_t ldb, b_estride;
+  const uint8_t* Be;  // E8M0 per expert: KN weights [K/32, N], KM weights [N, K/32]
+  int64_t lde_b, be_estride;
+  int N, K, kslots, f;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int2* tiles;
+  const int32_t* ntiles;
+  int gatherA;
+  const float* topk_w;
+  uint16_t* C0;
+  int64_t ldc0;
+  uint16_t* C1;
+  int64_t ldc1;
+  uint8_t* Q;   // requantised output codes (UP: As, DACT: dH)
+  int64_t ldq;
+  uint8_t* Qe;  // their E8M0 exponents, one per 32 columns
+  int64_t ldqe;
+  const uint16_t* Hs;
+  int64_t ldh;
+  float* dwp;
+  int nparts;
+};
+
+// Shared exponent s of a block with maximum magnitude amax: the smallest s with
+// amax <= 448 * 2^s, limited to [-127, 127]; 0 for an all-zero block.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ex;
+  (void)frexpf(amax, &ex);  // amax = m 2^ex, m in [0.5, 1)
+  int s = ex - 9;           // 2^(s+8) <= amax < 2^(s+9)
+  if (amax > ldexpf(448.0f, s)) ++s;
+  return min(max(s, -127), 127);
+}
+
+// Quantise 8 values of a 32-value block held by 4 consecutive lanes: returns the 8 e4m3 codes
+// and sets *e to the block's E8M0 byte.
+__device__ __forceinline__ u32x2 mx_quant8_group4(const float (&v)[8], uint32_t* e) {
+  float m = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  const int s = mx_exponent(m);
+  const float inv = ldexpf(1.0f, -s);  // exact: a power of two
+  *e = (uint32_t)(s + 127);
+  u32x2 q;
+  q.x = pack_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  q.y = pack_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  return q;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g) {
+  constexpr int BM = kFp8BM, BN = 256, BK = 128, S = 2, WM = 2, WN = 4, NW = 8, NTH = 512;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr bool B_KN = (MODE == X_UP || MODE == X_DOWN);
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, AE_BYTES = NW * 256, BE_BYTES = B_KN ? 4 * 256 : NW * 256;
+  constexpr int STAGE = A_BYTES + B_BYTES + AE_BYTES + BE_BYTES;
+  constexpr int QA = A_BYTES / (1024 * NW), QB = B_BYTES / (1024 * NW);
+  constexpr int CPAD = BN + 4;
+  constexpr int CBAND_BYTES = 2 * 32 * CPAD * 4;
+  constexpr int ARENA = S * STAGE > CBAND_BYTES ? S * STAGE : CBAND_BYTES;
+  static_assert(BM == 256 && QA == 4 && QB == 4, "DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[ARENA];
+  float* cband = reinterpret_cast<float*>(smem);
+  __shared__ float s_w[BM];
+  __shared__ int s_slot[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
+
+  // ------------------------------------------------------------------ tile coordinates
+  const int nN = (MODE == X_UP) ? g.f / (BN / 2) : g.N / BN;
+  const int G_valid = *(const CONST_AS int32_t*)g.ntiles * nN;
+  if ((int)blockIdx.x >= G_valid) return;
+  const int lid = xcd_remap(blockIdx.x, G_valid);
+  const int2 rc = grouped_tile(lid, G_valid / nN, nN, MX_GM);
+  const int nt = rc.y;
+  const int2 te = g.tiles[rc.x];
+  const int e = te.x;
+  const int m0 = g.offsets[e] + te.y * BM;
+  const int mrows = min(BM, g.offsets[e + 1] - m0);
+  const int n0 = (MODE == X_UP) ? nt * (BN / 2) : nt * BN;
+  for (int r = tid; r < BM; r += NTH) {
+    int p = -1;
+    float wv = 0.0f;
+    if (r < mrows) {
+      p = g.perm[m0 + r];
+      if (MODE == X_UP || MODE == X_DACT) wv = g.topk_w[p];
+    }
+    s_slot[r] = p;
+    s_w[r] = wv;
+  }
+  const uint8_t* Bexp = g.B + (int64_t)e * g.b_estride;
+  const uint8_t* Beexp = g.Be + (int64_t)e * g.be_estride;
+
+  // ------------------------------------------------------------------ DMA sources
+  // A (KM, 256 rows x 128 bytes): block gi = 4*wave + q holds rows 8*gi..8*gi+7.
+  const uint8_t* a_src[QA];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int row = 8 * (wave * QA + q) + lane / 8;
+    const int c = (lane % 8) ^ ((row >> 1) & 7);
+    const int pos = m0 + (row < mrows ? row : 0);  // rows past the expert feed unstored outputs
+    const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
+    a_src[q] = g.A + src * g.lda + 16 * c;
+  }
+  // A exponents: wave w brings the 4 bytes (k blocks of the stage) of rows 32w..32w+31; lanes
+  // past 31 repeat row 32w + 31.
+  const uint8_t* ae_src;
+  {
+    const int row = 32 * wave + min(lane, 31);
+    const int pos = m0 + (row < mrows ? row : 0);
+    const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
+    ae_src = g.Ae + src * g.lde_a;
+  }
+  const uint8_t* b_src[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    if constexpr (B_KN) {
+      const int kr = 4 * (wave * QB + q) + lane / 16;
+      const int c = (lane % 16) ^ (2 * (kr & 7));
+      int col;
+      if constexpr (MODE == X_UP) col = c < 8 ? n0 + 16 * c : g.f + n0 + 16 * (c - 8);
+      else col = n0 + 16 * c;
+      b_src[q] = Bexp + (int64_t)kr * g.ldb + col;
+    } else {
+      const int row = 8 * (wave * QB + q) + lane / 8;
+      const int c = (lane % 8) ^ ((row >> 1) & 7);
+      b_src[q] = Bexp + (int64_t)(n0 + row) * g.ldb + 16 * c;
+    }
+  }
+  // B exponents.  KN: rows kb = 4t..4t+3 of [K/32, N], 256 tile columns each; wave w < 4 brings
+  // row w, lane l columns 4l..4l+3 (UP: lanes < 32 gate, others up).  KM: like A, rows of W.
+  const uint8_t* be_src;
+  if constexpr (B_KN) {
+    int col;
+    if constexpr (MODE == X_UP) col = lane < 32 ? n0 + 4 * lane : g.f + n0 + 4 * (lane - 32);
+    else col = n0 + 4 * lane;
+    be_src = Beexp + (int64_t)(wave & 3) * g.lde_b + col;
+  } else {
+    be_src = Beexp + (int64_t)(n0 + 32 * wave + min(lane, 31)) * g.lde_b;
+  }
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    const int k0 = t * BK;
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, aebase = bbase + B_BYTES,
+                   bebase = aebase + AE_BYTES;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) dma16(a_src[q] + k0, abase + (wave * QA + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+      dma16(B_KN ? b_src[q] + (int64_t)k0 * g.ldb : b_src[q] + k0, bbase + (wave * QB + q) * 1024);
+    dma4(ae_src + 4 * t, aebase + wave * 256);
+    if constexpr (B_KN) {
+      if (wave < 4) dma4(be_src + (int64_t)(4 * t) * g.lde_b, bebase + wave * 256);
+    } else {
+      dma4(be_src + 4 * t, bebase + wave * 256);
+    }
+  };
+
+  auto b_row = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (MODE == X_UP)
+      return j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32;
+    else
+      return wn * TN + j * 32;
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Lane l of a 64-deep step kk gives the exponent of k block 2*kk + l/32 of the stage for its
+  // row (column); the fragments are read in the matching k order (read_k*8_mx).
+  const int kbsel = lane >> 5;
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, aebase = bbase + B_BYTES,
+                   bebase = aebase + AE_BYTES;
+    i32x8 bv[2][FN];
+    uint32_t sbw[2][FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = b_row(j) + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if constexpr (B_KN) bv[kk][j] = read_kn8_mx(bbase, b_row(j), kk, lane);
+        else bv[kk][j] = read_km8_mx(bbase, col, kk, lane);
+      }
+      if constexpr (B_KN) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          sbw[kk][j] = *(const LDS_AS uint8_t*)(uintptr_t)(bebase + (2 * kk + kbsel) * 256 + col);
+      } else {
+        const uint32_t dw = *(const LDS_AS uint32_t*)(uintptr_t)(bebase + (col >> 5) * 256 + (col & 31) * 4);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) sbw[kk][j] = (dw >> (8 * (2 * kk + kbsel))) & 0xFFu;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int arow = wm * TM + i * 32 + (lane & 31);
+      const uint32_t adw = *(const LDS_AS uint32_t*)(uintptr_t)(aebase + (arow >> 5) * 256 + (arow & 31) * 4);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const i32x8 af = read_km8_mx(abase, arow, kk, lane);
+        const int sa = (int)((adw >> (8 * (2 * kk + kbsel))) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bv[kk][j], acc[i][j], 0, 0, 0, sa, 0,
+                                                                      (int)sbw[kk][j]);
+      }
+    }
+  };
+
+  // ------------------------------------------------------------------ main loop (2 stages)
+  const int nk = g.K / BK;
+  __syncthreads();
+  issue(0, 0);
+  for (int it = 0; it < nk; ++it) {
+    vm_lgkm_wait_barrier<0>();
+    if (it + 1 < nk) issue(it + 1, (it + 1) % S);
+    compute(it % S);
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------------ epilogues (LDS band)
+  const int lcol = lane & 31;
+  constexpr int CH = BN / 8;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c = b_row(j) + lcol;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        cband[q * CPAD + c] = acc[i][j][r];
+      }
+    }
+    __syncthreads();
+    auto tile_row = [&](int q) __attribute__((always_inline)) { return (q >> 5) * TM + 32 * i + (q & 31); };
+    if constexpr (MODE == X_UP) {
+      // 16 lanes per row, 8 gate + 8 up columns each; 4 lanes form one 32-column block of As
+      for (int id = tid; id < 64 * (CH / 2); id += NTH) {
+        const int q = id / (CH / 2), cc = id % (CH / 2);
+        const int lr = tile_row(q);
+        const bool ok = lr < mrows;
+        const float* gp = &cband[q * CPAD + cc * 8];
+        const float* up = &cband[q * CPAD + BN / 2 + cc * 8];
+        const float w = s_w[lr];
+        float as[8];
+        uint32_t hg[4], hu[4], ab[4];
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+          const float g0 = gp[2 * t2], g1 = gp[2 * t2 + 1], u0 = up[2 * t2], u1 = up[2 * t2 + 1];
+          hg[t2] = pack_bf16x2(g0, g1);
+          hu[t2] = pack_bf16x2(u0, u1);
+          as[2 * t2] = w * g0 * sigmoidf_fast(g0) * u0;
+          as[2 * t2 + 1] = w * g1 * sigmoidf_fast(g1) * u1;
+          ab[t2] = pack_bf16x2(as[2 * t2], as[2 * t2 + 1]);
+        }
+        uint32_t ex;
+        const u32x2 qv = mx_quant8_group4(as, &ex);
+        if (ok) {
+          const int64_t pos = m0 + lr;
+          const int col = n0 + cc * 8;
+          *(uint4*)&g.C0[pos * g.ldc0 + col] = make_uint4(hg[0], hg[1], hg[2], hg[3]);
+          *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(hu[0], hu[1], hu[2], hu[3]);
+          *(uint4*)&g.C1[pos * g.ldc1 + col] = make_uint4(ab[0], ab[1], ab[2], ab[3]);
+          *(u32x2*)&g.Q[pos * g.ldq + col] = qv;
+          if ((cc & 3) == 0) g.Qe[pos * g.ldqe + col / 32] = (uint8_t)ex;
+        }
+      }
+    } else if constexpr (MODE == X_DACT) {
+      // 32 lanes per row (8 columns each): dSwiGLU, routing-weight partial, dH in bf16 and MXFP8
+      for (int id = tid; id < 64 * CH; id += NTH) {
+        const int q = id / CH, cc = id % CH;
+        const int lr = tile_row(q);
+        const bool ok = lr < mrows;
+        const int64_t pos = m0 + (ok ? lr : 0);
+        const int col = n0 + cc * 8;
+        const uint4 hgv = *(const uint4*)&g.Hs[pos * g.ldh + col];
+        const uint4 huv = *(const uint4*)&g.Hs[pos * g.ldh + g.f + col];
+        const float* Gp = &cband[q * CPAD + cc * 8];
+        const float w = s_w[lr];
+        float part = 0.0f, dg[8], du[8];
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+          const uint32_t wg = word_of(hgv, t2), wu = word_of(huv, t2);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float gv = hh ? hi_bf16(wg) : lo_bf16(wg), uv = hh ? hi_bf16(wu) : lo_bf16(wu);
+            const float G = Gp[2 * t2 + hh];
+            const float sg = sigmoidf_fast(gv), sl = gv * sg, da = w * G;
+            part += G * (sl * uv);
+            dg[2 * t2 + hh] = da * uv * sg * (1.0f + gv * (1.0f - sg));
+            du[2 * t2 + hh] = da * sl;
+          }
+        }
+        uint32_t eg, eu;
+        const u32x2 qg = mx_quant8_group4(dg, &eg);
+        const u32x2 qu = mx_quant8_group4(du, &eu);
+#pragma unroll
+        for (int m = CH / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+        if (ok) {
+          *(uint4*)&g.C0[pos * g.ldc0 + col] = make_uint4(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
+                                                          pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7]));
+          *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
+                                                                pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7]));
+          *(u32x2*)&g.Q[pos * g.ldq + col] = qg;
+          *(u32x2*)&g.Q[pos * g.ldq + g.f + col] = qu;
+          if ((cc & 3) == 0) {
+            g.Qe[pos * g.ldqe + col / 32] = (uint8_t)eg;
+            g.Qe[pos * g.ldqe + (g.f + col) / 32] = (uint8_t)eu;
+          }
+          if (cc == 0) g.dwp[pos * g.nparts + nt] = part;
+        }
+      }
+    } else {
+      for (int id = tid; id < 64 * CH; id += NTH) {
+        const int q = id / CH, cc = id % CH;
+        const int lr = tile_row(q);
+        if (lr < mrows) {
+          const float* cp = &cband[q * CPAD + cc * 8];
+          const uint4 o = make_uint4(pack_bf16x2(cp[0], cp[1]), pack_bf16x2(cp[2], cp[3]),
+                                     pack_bf16x2(cp[4], cp[5]), pack_bf16x2(cp[6], cp[7]));
+          *(uint4*)&g.C0[(int64_t)s_slot[lr] * g.ldc0 + n0 + cc * 8] = o;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------- quantisers
+// Row blocks: src bf16 [rows, cols] -> codes [rows, cols], exponents [rows, cols/32]; four
+// threads per 32-value block, eight values each.
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __restrict__ src, int64_t n8, int cols,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ qe) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool ok = i < n8;
+  const int64_t ii = ok ? i : 0;
+  const uint4 v = *(const uint4*)(src + ii * 8);
+  float f[8] = {lo_bf16(v.x), hi_bf16(v.x), lo_bf16(v.y), hi_bf16(v.y),
+                lo_bf16(v.z), hi_bf16(v.z), lo_bf16(v.w), hi_bf16(v.w)};
+  uint32_t ex;
+  const u32x2 qv = mx_quant8_group4(f, &ex);
+  if (ok) {
+    *(u32x2*)(q + ii * 8) = qv;
+    if ((ii & 3) == 0) qe[(ii * 8) / 32] = (uint8_t)ex;  // cols % 32 == 0: blocks never straddle rows
+  }
+}
+
+// Column blocks within each matrix of a batch: src bf16 [batch, rows, cols] -> codes of the same
+// shape, exponents [batch, rows/32, cols].  One thread per 32 rows x 8 columns.
+__global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __restrict__ src, int64_t nunits,
+                                                            int rows, int cols, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ qe) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= nunits) return;
+  const int c8 = cols / 8;
+  const int64_t per_mat = (int64_t)(rows / 32) * c8;
+  const int64_t b = u / per_mat;
+  const int64_t rem = u % per_mat;
+  const int rb = (int)(rem / c8), cc = (int)(rem % c8);
+  const int64_t base = (b * rows + (int64_t)rb * 32) * cols + cc * 8;
+  float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = 0; r < 32; ++r) {
+    const uint4 v = *(const uint4*)(src + base + (int64_t)r * cols);
+    const float f[8] = {lo_bf16(v.x), hi_bf16(v.x), lo_bf16(v.y), hi_bf16(v.y),
+                        lo_bf16(v.z), hi_bf16(v.z), lo_bf16(v.w), hi_bf16(v.w)};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) amax[t] = fmaxf(amax[t], fabsf(f[t]));
+  }
+  int s[8];
+  float inv[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    s[t] = mx_exponent(amax[t]);
+    inv[t] = ldexpf(1.0f, -s[t]);
+  }
+  for (int r = 0; r < 32; ++r) {
+    const uint4 v = *(const uint4*)(src + base + (int64_t)r * cols);
+    const float f[8] = {lo_bf16(v.x), hi_bf16(v.x), lo_bf16(v.y), hi_bf16(v.y),
+                        lo_bf16(v.z), hi_bf16(v.z), lo_bf16(v.w), hi_bf16(v.w)};
+    u32x2 o;
+    o.x = pack_e4m3x4(f[0] * inv[0], f[1] * inv[1], f[2] * inv[2], f[3] * inv[3]);
+    o.y = pack_e4m3x4(f[4] * inv[4], f[5] * inv[5], f[6] * inv[6], f[7] * inv[7]);
+    *(u32x2*)(q + base + (int64_t)r * cols) = o;
+  }
+  uint8_t* eo = qe + (b * (rows / 32) + rb) * (int64_t)cols + cc * 8;
+  u32x2 ev;
+  ev.x = (uint32_t)(s[0] + 127) | ((uint32_t)(s[1] + 127) << 8) | ((uint32_t)(s[2] + 127) << 16) |
+         ((uint32_t)(s[3] + 127) << 24);
+  ev.y = (uint32_t)(s[4] + 127) | ((uint32_t)(s[5] + 127) << 8) | ((uint32_t)(s[6] + 127) << 16) |
+         ((uint32_t)(s[7] + 127) << 24);
+  *(u32x2*)eo = ev;
+}
+
+hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int cols, int along_rows, uint8_t* q,
+                           uint8_t* qe, hipStream_t st) {
+  if (batch * rows * cols == 0) return hipSuccess;
+  if (!along_rows) {  // blocks of 32 consecutive values of a row
+    const int64_t n8 = batch * rows * (int64_t)cols / 8;
+    mx_quant_rows_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(src, n8, cols, q, qe);
+  } else {            // blocks of 32 consecutive rows of a column
+    const int64_t nunits = batch * (int64_t)(rows / 32) * (cols / 8);
+    mx_quant_cols_kernel<<<(unsigned)((nunits + 255) / 256), 256, 0, st>>>(src, nunits, rows, cols, q, qe);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------- GEMM launchers
+namespace {
+template <int MODE>
+hipError_t run_mx(const MxArgs& g, int64_t A, int E, int nN, hipStream_t st) {
+  const int64_t blocks = (int64_t)max_row_tiles(A, E, kFp8BM) * nN;
+  if (blocks == 0) return hipSuccess;
+  grouped_gemm_mx_kernel<MODE><<<(unsigned)blocks, 512, 0, st>>>(g);
+  return hipGetLastError();
+}
+MxArgs mx_base(const MoeShape& s, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+               const int32_t* ntiles) {
+  MxArgs g{};
+  g.kslots = s.k;
+  g.f = s.f;
+  g.offsets = offsets;
+  g.perm = perm;
+  g.tiles = tiles;
+  g.ntiles = ntiles;
+  return g;
+}
+}  // namespace
+
+hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe, const uint8_t* W1q,
+                        const uint8_t* W1e, const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                        const int2* tiles, const int32_t* ntiles, uint16_t* H, uint16_t* As, uint8_t* Asq,
+                        uint8_t* Ase, hipStream_t st) {
+  MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
+  g.A = xq;
+  g.lda = s.d;
+  g.Ae = xe;
+  g.lde_a = s.d / 32;
+  g.gatherA = 1;
+  g.B = W1q;  // [E, d, 2f], column blocks: exponents [E, d/32, 2f]
+  g.ldb = 2 * (int64_t)s.f;
+  g.b_estride = (int64_t)s.d * 2 * s.f;
+  g.Be = W1e;
+  g.lde_b = 2 * (int64_t)s.f;
+  g.be_estride = (int64_t)(s.d / 32) * 2 * s.f;
+  g.N = 2 * s.f;
+  g.K = s.d;
+  g.topk_w = topk_w;
+  g.C0 = H;
+  g.ldc0 = 2 * (int64_t)s.f;
+  g.C1 = As;
+  g.ldc1 = s.f;
+  g.Q = Asq;
+  g.ldq = s.f;
+  g.Qe = Ase;
+  g.ldqe = s.f / 32;
+  return run_mx<X_UP>(g, (int64_t)s.T * s.k, s.E, s.f / 128, st);
+}
+
+hipError_t launch_mx_down(const MoeShape& s, const uint8_t* Asq, const uint8_t* Ase, const uint8_t* W2q,
+                          const uint8_t* W2e, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                          const int32_t* ntiles, uint16_t* Op, hipStream_t st) {
+  MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
+  g.A = Asq;
+  g.lda = s.f;
+  g.Ae = Ase;
+  g.lde_a = s.f / 32;
+  g.B = W2q;  // [E, f, d], column blocks: exponents [E, f/32, d]
+  g.ldb = s.d;
+  g.b_estride = (int64_t)s.f * s.d;
+  g.Be = W2e;
+  g.lde_b = s.d;
+  g.be_estride = (int64_t)(s.f / 32) * s.d;
+  g.N = s.d;
+  g.K = s.f;
+  g.C0 = Op;
+  g.ldc0 = s.d;
+  return run_mx<X_DOWN>(g, (int64_t)s.T * s.k, s.E, s.d / 256, st);
+}
+
+hipError_t launch_mx_dact(const MoeShape& s, const uint8_t* dyq, const uint8_t* dye, const uint8_t* W2q,
+                          const uint8_t* W2e, const uint16_t* H, const float* topk_w, const int32_t* offsets,
+                          const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* dH, uint8_t* dHq,
+                          uint8_t* dHe, float* dwp, hipStream_t st) {
+  MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
+  g.A = dyq;
+  g.lda = s.d;
+  g.Ae = dye;
+  g.lde_a = s.d / 32;
+  g.gatherA = 1;
+  g.B = W2q;  // [E, f, d], row blocks (K = d): exponents [E, f, d/32]
+  g.ldb = s.d;
+  g.b_estride = (int64_t)s.f * s.d;
+  g.Be = W2e;
+  g.lde_b = s.d / 32;
+  g.be_estride = (int64_t)s.f * (s.d / 32);
+  g.N = s.f;
+  g.K = s.d;
+  g.topk_w = topk_w;
+  g.Hs = H;
+  g.ldh = 2 * (int64_t)s.f;
+  g.C0 = dH;
+  g.ldc0 = 2 * (int64_t)s.f;
+  g.Q = dHq;
+  g.ldq = 2 * (int64_t)s.f;
+  g.Qe = dHe;
+  g.ldqe = 2 * s.f / 32;
+  g.dwp = dwp;
+  g.nparts = s.f / 256;
+  return run_mx<X_DACT>(g, (int64_t)s.T * s.k, s.E, s.f / 256, st);
+}
+
+hipError_t launch_mx_dx(const MoeShape& s, const uint8_t* dHq, const uint8_t* dHe, const uint8_t* W1q,
+                        const uint8_t* W1e, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                        const int32_t* ntiles, uint16_t* dXp, hipStream_t st) {
+  MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
+  g.A = dHq;
+  g.lda = 2 * (int64_t)s.f;
+  g.Ae = dHe;
+  g.lde_a = 2 * s.f / 32;
+  g.B = W1q;  // [E, d, 2f], row blocks (K = 2f): exponents [E, d, 2f/32]
+  g.ldb = 2 * (int64_t)s.f;
+  g.b_estride = (int64_t)s.d * 2 * s.f;
+  g.Be = W1e;
+  g.lde_b = 2 * s.f / 32;
+  g.be_estride = (int64_t)s.d * (2 * s.f / 32);
+  g.N = s.d;
+  g.K = 2 * s.f;
+  g.C0 = dXp;
+  g.ldc0 = s.d;
+  return run_mx<X_DX>(g, (int64_t)s.T * s.k, s.E, s.d / 256, st);
+}
+
+}  // namespace moe

@@ -97,6 +97,26 @@ hipError_t launch_quant_rows(const uint16_t* src, int64_t rows, int cols, uint8_
 hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, int cols, uint16_t* dst,
                                hipStream_t st);
 
+// MXFP8: e4m3 codes with one E8M0 exponent byte per 32 values along each GEMM's K.
+// along_rows = 0: blocks of 32 consecutive values of a row -> exponents [batch, rows, cols/32];
+// along_rows = 1: blocks of 32 consecutive rows of a column -> exponents [batch, rows/32, cols].
+hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int cols, int along_rows, uint8_t* q,
+                           uint8_t* qe, hipStream_t st);
+hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe, const uint8_t* W1q,
+                        const uint8_t* W1e, const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                        const int2* tiles, const int32_t* ntiles, uint16_t* H, uint16_t* As, uint8_t* Asq,
+                        uint8_t* Ase, hipStream_t st);
+hipError_t launch_mx_down(const MoeShape& s, const uint8_t* Asq, const uint8_t* Ase, const uint8_t* W2q,
+                          const uint8_t* W2e, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                          const int32_t* ntiles, uint16_t* Op, hipStream_t st);
+hipError_t launch_mx_dact(const MoeShape& s, const uint8_t* dyq, const uint8_t* dye, const uint8_t* W2q,
+                          const uint8_t* W2e, const uint16_t* H, const float* topk_w, const int32_t* offsets,
+                          const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* dH, uint8_t* dHq,
+                          uint8_t* dHe, float* dwp, hipStream_t st);
+hipError_t launch_mx_dx(const MoeShape& s, const uint8_t* dHq, const uint8_t* dHe, const uint8_t* W1q,
+                        const uint8_t* W1e, const int32_t* offsets, const int32_t* perm, const int2* tiles,
+                        const int32_t* ntiles, uint16_t* dXp, hipStream_t st);
+
 // data movement and router backward
 hipError_t launch_permute(const uint16_t* x, const int32_t* perm, const int32_t* offsets, int64_t A, int d, int k,
                           uint16_t* xp, hipStream_t st);

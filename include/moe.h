@@ -41,10 +41,19 @@
  *   - Errors: a negative MOE_ERR_* code is returned and nothing is enqueued; MOE_ERR_HIP means
  *     a launch failed (moe_status_string() then names the HIP error).
  *   - Shapes (MOE_ERR_SHAPE otherwise): T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64),
- *     d and f positive multiples of 128 (MOE_FP8_E4M3: of 256) and at most 65536, T*k < 2^31.
+ *     d and f positive multiples of 128 (MOE_FP8_E4M3, MOE_MXFP8: of 256) and at most 65536,
+ *     T*k < 2^31.
  *   - fp8 (MOE_FP8_E4M3): codes are OCP e4m3 (bias 7, max 448, no infinities); a block's value
  *     is code * scale with its fp32 scale ([Prime] "Mit csinált a Prime Intellect?": blockwise
  *     FP8 is one of the kernel's data types).  Outputs and gradients stay bf16/fp32.
+ *   - MXFP8 (MOE_MXFP8): x, W1, W2 are passed in bf16 (the 16-bit master copies) and the
+ *     library quantises them on every call to OCP MXFP8 (e4m3 codes, one E8M0 exponent per 32
+ *     values along each GEMM's K; [JAX] "Csoportosított mátrixszorzás és összevont
+ *     adatmozgatás": group-aware MXFP8 quantisation feeding an MXFP8 grouped GEMM; [TE]
+ *     "צמצום הזיכרון ותקורות הכימות": one scale per 32 values).  The exponent of a block is the
+ *     smallest power of two that brings its maximum magnitude within 448 (no clipping); elements
+ *     round to nearest even.  The data-gradient GEMMs use weights quantised along their own K.
+ *     Weight gradients are computed from bf16 operands.  d and f must be multiples of 256.
  *   - Alignment (MOE_ERR_ALIGN otherwise): tensors 16-byte aligned, ws and saved 256-byte
  *     aligned (every torch/hipMalloc allocation is).
  */
@@ -58,7 +67,7 @@
 extern "C" {
 #endif
 
-typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1 } moe_dtype;
+typedef enum { MOE_BF16 = 0, MOE_FP8_E4M3 = 1, MOE_MXFP8 = 2 } moe_dtype;
 
 typedef struct {
   int64_t T, d, f, E, k;
@@ -162,6 +171,16 @@ typedef void (*moe_stage_hook)(const char* stage, int begin, void* stream, void*
 int moe_set_stage_hook(moe_stage_hook hook, void* user);
 
 /* Static string for a status code (for MOE_ERR_HIP: the last HIP error on this thread). */
+/* MXFP8 quantisation on its own (the same kernels the MOE_MXFP8 path runs).  src is bf16
+ * [batch, rows, cols] (row-major).  block_axis = 1: each block is 32 consecutive values of a row
+ * (cols % 32 == 0), exps is [batch, rows, cols/32]; block_axis = 0: each block is 32
+ * consecutive rows of one column (rows % 32 == 0, cols % 8 == 0), exps is [batch, rows/32,
+ * cols].  codes (e4m3) has src's shape; exps are E8M0 bytes (2^(E-127)).  Rules as for
+ * MOE_MXFP8 above.  Tensors 16-byte aligned.  ([JAX] "Csoportosított mátrixszorzás és
+ * összevont adatmozgatás": group-aware MXFP8 quantisation.) */
+int moe_mxfp8_quantize(const void* src, int64_t batch, int64_t rows, int64_t cols, int block_axis, void* codes,
+                       void* exps, void* stream);
+
 const char* moe_status_string(int status);
 
 #ifdef __cplusplus

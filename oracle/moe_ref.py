@@ -136,14 +136,23 @@ def forward(x, W1, W2, ids, w, E=None, return_saved=False):
 
 
 # ------------------------------------------------------------------------------ backward
-def backward(x, W1, W2, ids, w, dy, logits_routed=True):
+def backward(x, W1, W2, ids, w, dy, logits_routed=True, W1_dx=None, W2_da=None, dy_da=None, x_dw=None):
     """Gradients of L = sum(dy * y) for the forward above.
 
     Returns dict with dx [T,d], dW1 [E,d,2f], dW2 [E,f,d], d_topk_w [T,k] (0 on unrouted
     slots) and, when the weights came from route() (logits_routed=True), d_logits [T,E]
-    through the softmax over the k selected logits (0 off the selected set)."""
+    through the softmax over the k selected logits (0 off the selected set).
+
+    The optional operands name a different copy of a tensor for one product, as a quantised
+    layer has when each GEMM quantises along its own K (MXFP8): dy_da and W2_da for
+    da = (w dy) W2^T and the routing-weight gradient, W1_dx for dx = dH W1^T, x_dw for
+    dW1 = x^T dH.  Left as None they are dy, W2, W1 and x."""
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
+    W1_dx = W1 if W1_dx is None else W1_dx
+    W2_da = W2 if W2_da is None else W2_da
+    dy_da = dy if dy_da is None else np.asarray(dy_da, np.float64)
+    x_dw = x if x_dw is None else np.asarray(x_dw, np.float64)
     T, d = x.shape
     E = W1.shape[0]
     f = W2.shape[1]
@@ -164,17 +173,15 @@ def backward(x, W1, W2, ids, w, dy, logits_routed=True):
         sg = _sigmoid(G)
         S = G * sg                                     # silu(g)
         a = S * U
-        Oe = a @ W2[e]
-        dYe = dy[R]
-        dw[P] = np.sum(dYe * Oe, axis=1)               # y is linear in each routing weight
-        dOe = wf[P][:, None] * dYe
-        dW2[e] = a.T @ dOe
-        da = dOe @ W2[e].T
+        dYa = dy_da[R]
+        dw[P] = np.sum(dYa * (a @ W2_da[e]), axis=1)   # y is linear in each routing weight
+        dW2[e] = a.T @ (wf[P][:, None] * dy[R])
+        da = (wf[P][:, None] * dYa) @ W2_da[e].T
         dG = da * U * sg * (1.0 + G * (1.0 - sg))      # d silu / dg = sig * (1 + g (1 - sig))
         dU = da * S
         dH = np.concatenate([dG, dU], axis=1)
-        dW1[e] = Xe.T @ dH
-        np.add.at(dx, R, dH @ W1[e].T)
+        dW1[e] = x_dw[R].T @ dH
+        np.add.at(dx, R, dH @ W1_dx[e].T)
     out = dict(dx=dx, dW1=dW1, dW2=dW2, d_topk_w=dw.reshape(T, k), plan=pl)
     if logits_routed:
         wm = np.asarray(w, np.float64)

@@ -40,10 +40,14 @@ def rel_err(gpu, ref) -> float:
 class GpuLayer:
     """Device copies of one layer's inputs plus every buffer the library needs."""
 
-    def __init__(self, inp, device="cuda", backward=True):
+    def __init__(self, inp, device="cuda", backward=True, dtype=None):
+        """dtype: the layer's moe dtype; defaults to the inputs' format (bf16 inputs may also
+        run as MOE_MXFP8, which quantises them inside the library)."""
         self.inp = inp
         self.fp8 = inp.dtype == "fp8"
-        self.dm = moe.dims(inp.T, inp.d, inp.f, inp.E, inp.k, moe.MOE_FP8_E4M3 if self.fp8 else moe.MOE_BF16)
+        if dtype is None:
+            dtype = moe.MOE_FP8_E4M3 if self.fp8 else moe.MOE_BF16
+        self.dm = moe.dims(inp.T, inp.d, inp.f, inp.E, inp.k, dtype)
         if self.fp8:
             self.x, self.W1, self.W2 = (torch.from_numpy(np.ascontiguousarray(a)).to(device)
                                         for a in (inp.x, inp.W1, inp.W2))

@@ -1,0 +1,81 @@
+"""GPU checks of the MXFP8 path: the quantisers bit for bit against the oracle's MX quantiser
+(same blocks, same exponent rule, same rounding), and the layer against the fp64 oracle run on
+the MX-quantised inputs (x and dy in row blocks along d; W1, W2 in blocks along each GEMM's K)."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_gemm_expert_router_amd as moe
+import oracle
+from workloads import make_inputs
+from moe_testlib import GpuLayer, TOL_FP8, bf16_dev, rel_err, to_np, check_routing_bitexact
+
+pytestmark = pytest.mark.gpu
+
+
+def _values(codes):
+    # +0 and -0 are the same value; compare decoded values where codes may differ only in that
+    return oracle.e4m3_to_f64(codes)
+
+
+@pytest.mark.parametrize("shape,axis", [((3, 64, 96), 1), ((2, 96, 64), 0), ((1, 40, 2048), 1), ((4, 256, 80), 0)])
+def test_mx_quantize_bitexact(shape, axis):
+    g = np.random.default_rng(sum(shape) + axis)
+    v = (g.normal(0, 1, shape) * np.exp2(g.integers(-8, 8, shape[:1] + (1, 1)))).astype(np.float32)
+    v.reshape(-1)[:40] = 0.0                                  # an all-zero block at the start
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)       # truncation to bf16 is fine: it is the input
+    src = bf16_dev(bits)
+    codes = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    eshape = (shape[0], shape[1], shape[2] // 32) if axis == 1 else (shape[0], shape[1] // 32, shape[2])
+    exps = torch.empty(eshape, dtype=torch.uint8, device="cuda")
+    print(f"[case] mx quantize {shape} block_axis={axis}", flush=True)
+    moe.moe_mxfp8_quantize(src, shape[0], shape[1], shape[2], axis, codes, exps)
+    torch.cuda.synchronize()
+    rc, re = oracle.mx_quantize(oracle.bf16_to_f64(bits), axis=2 if axis == 1 else 1)
+    np.testing.assert_array_equal(exps.cpu().numpy(), re)
+    np.testing.assert_array_equal(_values(codes.cpu().numpy()), _values(rc))
+
+
+def _mx_oracle(inp):
+    """fp64 layer on the MX-quantised operands, with the same quantisation points as the GPU
+    path except the intermediates (As, dH), which the oracle keeps exact."""
+    x = oracle.bf16_to_f64(inp.x)
+    W1 = oracle.bf16_to_f64(inp.W1)
+    W2 = oracle.bf16_to_f64(inp.W2)
+    dy = oracle.bf16_to_f64(inp.dy)
+    q = lambda v, ax: oracle.mx_dequantize(*oracle.mx_quantize(v, ax), ax)
+    xq, W1f, W2f = q(x, 1), q(W1, 1), q(W2, 1)          # forward: K = d, f
+    dyq, W1b, W2b = q(dy, 1), q(W1, 2), q(W2, 2)         # data gradients: K = d, 2f
+    ids, w = oracle.route(inp.logits, inp.k)
+    y = oracle.forward(xq, W1f, W2f, ids, w)
+    # H from the forward's operands; dA from dy and W2 in blocks along d; dX with W1 in blocks
+    # along 2f; the weight gradients multiply the bf16 x and dy
+    bw = oracle.backward(xq, W1f, W2f, ids, w, dy, W1_dx=W1b, W2_da=W2b, dy_da=dyq, x_dw=x)
+    return dict(ids=ids, w=w, plan=bw["plan"], y=y, dx=bw["dx"], d_topk_w=bw["d_topk_w"], d_logits=bw["d_logits"],
+                dW1=bw["dW1"], dW2=bw["dW2"])
+
+
+CASES = {"mx_small": (160, 256, 256, 8, 2, 41), "mx_wide": (300, 512, 768, 6, 3, 42)}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_mx_layer_parity(name):
+    T, d, f, E, k, seed = CASES[name]
+    inp = make_inputs(T, d, f, E, k, seed=seed)
+    print(f"[case] {name} T={T} d={d} f={f} E={E} k={k}", flush=True)
+    gl = GpuLayer(inp, dtype=moe.MOE_MXFP8).run()
+    ref = _mx_oracle(inp)
+    check_routing_bitexact(gl, ref["ids"], ref["plan"])
+    b = gl.b
+    errs = {"y": rel_err(to_np(b["y"]), ref["y"]), "dx": rel_err(to_np(b["dx"]), ref["dx"]),
+            "d_topk_w": rel_err(to_np(b["d_topk_w"]), ref["d_topk_w"]),
+            "d_logits": rel_err(to_np(b["d_logits"]), ref["d_logits"])}
+    dW1, dW2 = to_np(b["dW1"]), to_np(b["dW2"])
+    for e in range(E):
+        if ref["plan"].counts[e]:
+            errs[f"dW1[{e}]"] = rel_err(dW1[e], ref["dW1"][e])
+            errs[f"dW2[{e}]"] = rel_err(dW2[e], ref["dW2"][e])
+    print(f"[case] {name}: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items() if not k.startswith("dW")) +
+          f", max dW {max(v for k, v in errs.items() if k.startswith('dW')):.2e}", flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL_FP8}
+    assert not bad, bad

@@ -117,3 +117,32 @@ def test_mx_roundtrip_of_representable_values_and_error_bound():
     back = oracle.mx_dequantize(cw, sw, axis=1)
     big = np.abs(w) >= np.repeat(oracle.e8m0_to_f64(sw), 32, axis=1) * 2.0 ** -6
     assert np.all(np.abs(back - w)[big] <= np.abs(w)[big] * 2.0 ** -4)
+
+
+def test_backward_with_separate_operand_copies():
+    """The optional operand copies reduce to the plain backward when they are the same arrays,
+    and each one only enters its own product."""
+    g = np.random.default_rng(5)
+    T, d, f, E, k = 12, 8, 6, 3, 2
+    x, dy = g.normal(size=(T, d)), g.normal(size=(T, d))
+    W1, W2 = g.normal(size=(E, d, 2 * f)) / 3, g.normal(size=(E, f, d)) / 3
+    L = g.normal(size=(T, E))
+    ids, w = oracle.route(L, k)
+    base = oracle.backward(x, W1, W2, ids, w, dy)
+    same = oracle.backward(x, W1, W2, ids, w, dy, W1_dx=W1, W2_da=W2, dy_da=dy, x_dw=x)
+    for key in ("dx", "dW1", "dW2", "d_topk_w", "d_logits"):
+        np.testing.assert_array_equal(base[key], same[key])
+    # W1_dx enters dx only (linearly): doubling it doubles dx and leaves the rest unchanged
+    dbl = oracle.backward(x, W1, W2, ids, w, dy, W1_dx=2 * W1)
+    np.testing.assert_allclose(dbl["dx"], 2 * base["dx"], rtol=1e-12, atol=1e-12)
+    for key in ("dW1", "dW2", "d_topk_w"):
+        np.testing.assert_array_equal(dbl[key], base[key])
+    # x_dw enters dW1 only
+    dbx = oracle.backward(x, W1, W2, ids, w, dy, x_dw=3 * x)
+    np.testing.assert_allclose(dbx["dW1"], 3 * base["dW1"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(dbx["dx"], base["dx"])
+    # dy_da scales da and the routing-weight gradient, not dW2
+    dby = oracle.backward(x, W1, W2, ids, w, dy, dy_da=2 * dy)
+    np.testing.assert_allclose(dby["d_topk_w"], 2 * base["d_topk_w"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dby["dx"], 2 * base["dx"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(dby["dW2"], base["dW2"])
