@@ -210,9 +210,13 @@ def token_forward(x_row, W1, W2, ids_row, w_row):
     return y
 
 
-def token_backward(x_row, W1, W2, ids_row, w_row, dy_row):
-    """(dx[t], d_topk_w[t, :]) for one token."""
+def token_backward(x_row, W1, W2, ids_row, w_row, dy_row, W1_dx=None, W2_da=None, dy_da=None):
+    """(dx[t], d_topk_w[t, :]) for one token.  W1_dx, W2_da and dy_da name other copies of
+    W1, W2 and dy for the products dx = dH W1^T and da = w dy W2^T, as in backward()."""
     f = W2.shape[1]
+    W1_dx = W1 if W1_dx is None else W1_dx
+    W2_da = W2 if W2_da is None else W2_da
+    dy_da = dy_row if dy_da is None else dy_da
     dx = np.zeros(x_row.shape[0])
     dw = np.zeros(len(ids_row))
     for j, (e, wj) in enumerate(zip(ids_row, w_row)):
@@ -223,11 +227,11 @@ def token_backward(x_row, W1, W2, ids_row, w_row, dy_row):
         sg = _sigmoid(g)
         s = g * sg
         a = s * u
-        dw[j] = dy_row @ (a @ W2[e])
-        da = wj * (W2[e] @ dy_row)
+        dw[j] = dy_da @ (a @ W2_da[e])
+        da = wj * (W2_da[e] @ dy_da)
         dg = da * u * sg * (1.0 + g * (1.0 - sg))
         du = da * s
-        dx += W1[e] @ np.concatenate([dg, du])
+        dx += W1_dx[e] @ np.concatenate([dg, du])
     return dx, dw
 
 

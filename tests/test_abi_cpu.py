@@ -142,3 +142,24 @@ def test_forward_backward_argument_errors(lib):
     assert lib.moe_combine(ctypes.byref(dm), None, F, F, None) == moe.MOE_ERR_NULL
     assert lib.moe_permute(ctypes.byref(dm), F, F, F, None, None) == moe.MOE_ERR_NULL
     assert lib.moe_combine(ctypes.byref(dm), F + 4, F, F, None) == moe.MOE_ERR_ALIGN
+
+
+def test_mxfp8_argument_rules(lib):
+    F = FAKE
+    mx = moe.dims(64, 256, 256, 8, 2, dtype=moe.MOE_MXFP8)
+    rc, wf = sz(lib, mx, moe.MOE_WS_FORWARD)
+    assert rc == 0
+    # MXFP8 takes bf16 inputs and quantises them itself: scales must be NULL
+    assert lib.moe_forward(ctypes.byref(mx), F, F, F, None, F, None, F, F, F, F, F, F, F, wf, None) == moe.MOE_ERR_DTYPE
+    # workspace holds the quantised copies: larger than the bf16 layer's
+    bf = moe.dims(64, 256, 256, 8, 2)
+    assert wf > sz(lib, bf, moe.MOE_WS_FORWARD)[1] + 8 * 256 * 512   # at least W1's e4m3 codes
+    assert sz(lib, moe.dims(64, 128, 256, 8, 2, dtype=moe.MOE_MXFP8), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
+    q = lambda *a: lib.moe_mxfp8_quantize(*a, None)
+    assert q(F, 1, 64, 100, 1, F, F) == moe.MOE_ERR_SHAPE      # row blocks need cols % 32 == 0
+    assert q(F, 1, 40, 64, 0, F, F) == moe.MOE_ERR_SHAPE       # column blocks need rows % 32 == 0
+    assert q(F, 1, 64, 60, 0, F, F) == moe.MOE_ERR_SHAPE       # ... and cols % 8 == 0
+    assert q(F, 1, 64, 64, 2, F, F) == moe.MOE_ERR_SHAPE       # block_axis is 0 or 1
+    assert q(None, 1, 64, 64, 1, F, F) == moe.MOE_ERR_NULL
+    assert q(F, 1, 64, 64, 1, F + 8, F) == moe.MOE_ERR_ALIGN
+    assert q(F, 0, 64, 64, 1, None, None) == moe.MOE_OK         # empty input: nothing to do

@@ -79,3 +79,57 @@ def test_mx_layer_parity(name):
           f", max dW {max(v for k, v in errs.items() if k.startswith('dW')):.2e}", flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL_FP8}
     assert not bad, bad
+
+
+class _MxExperts:
+    """W[e] MX-quantised along `axis` of the expert matrix and dequantised to fp64 on first use
+    (a few experts kept), so the full-size check never holds every expert in fp64."""
+
+    def __init__(self, Wbits, axis, keep=4):
+        from collections import OrderedDict
+        self.W, self.axis, self.keep = Wbits, axis, keep
+        self.shape = Wbits.shape
+        self.cache = OrderedDict()
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            v = oracle.bf16_to_f64(self.W[e])
+            self.cache[e] = oracle.mx_dequantize(*oracle.mx_quantize(v, self.axis), self.axis)
+            if len(self.cache) > self.keep:
+                self.cache.popitem(last=False)
+        self.cache.move_to_end(e)
+        return self.cache[e]
+
+
+@pytest.mark.slow
+def test_mx_fullsize_qwen3():
+    from workloads import make_config
+    inp = make_config("qwen3")
+    print(f"[case] full-size qwen3 as MXFP8: T={inp.T} d={inp.d} f={inp.f} E={inp.E} k={inp.k}", flush=True)
+    gl = GpuLayer(inp, dtype=moe.MOE_MXFP8).run()
+    ids, w = oracle.route(inp.logits, inp.k)
+    check_routing_bitexact(gl, ids, oracle.plan(ids, inp.E))
+    g = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([[0, inp.T - 1], g.choice(inp.T, 8, replace=False)]))
+    q = lambda v: oracle.mx_dequantize(*oracle.mx_quantize(v, 0), 0)
+    W1f, W2f = _MxExperts(inp.W1, 0), _MxExperts(inp.W2, 0)      # blocks along d / f (forward K)
+    W1b, W2b = _MxExperts(inp.W1, 1), _MxExperts(inp.W2, 1)      # blocks along 2f / d (data-gradient K)
+    b = gl.b
+    y_o, dx_o, dw_o = [], [], []
+    for t in toks:
+        xq = q(oracle.bf16_to_f64(inp.x[t]))
+        dyq = q(oracle.bf16_to_f64(inp.dy[t]))
+        y_o.append(oracle.token_forward(xq, W1f, W2f, ids[t], w[t]))
+        dxt, dwt = oracle.token_backward(xq, W1f, W2f, ids[t], w[t], dyq, W1_dx=W1b, W2_da=W2b, dy_da=dyq)
+        dx_o.append(dxt)
+        dw_o.append(dwt)
+    errs = {"y": rel_err(to_np(b["y"])[toks], np.stack(y_o)), "dx": rel_err(to_np(b["dx"])[toks], np.stack(dx_o)),
+            "d_topk_w": rel_err(to_np(b["d_topk_w"])[toks], np.stack(dw_o))}
+    # y is linear in the routing weights: sum(dy * y) ~ sum(w * d_topk_w) up to the quantisation of dy
+    lhs = float((gl.dy.double() * b["y"].double()).sum())
+    mid = float((b["topk_w"].double() * b["d_topk_w"].double()).sum())
+    errs["sum(w*dw)"] = abs(mid - lhs) / float(gl.dy.double().abs().mul(b["y"].double().abs()).sum())
+    print("[case] qwen3 MXFP8: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL_FP8}
+    assert not bad, bad

@@ -146,3 +146,17 @@ def test_backward_with_separate_operand_copies():
     np.testing.assert_allclose(dby["d_topk_w"], 2 * base["d_topk_w"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dby["dx"], 2 * base["dx"], rtol=1e-12, atol=1e-12)
     np.testing.assert_array_equal(dby["dW2"], base["dW2"])
+
+
+def test_token_backward_with_copies_matches_full_backward():
+    g = np.random.default_rng(6)
+    T, d, f, E, k = 10, 8, 6, 3, 2
+    x, dy = g.normal(size=(T, d)), g.normal(size=(T, d))
+    W1, W2 = g.normal(size=(E, d, 2 * f)) / 3, g.normal(size=(E, f, d)) / 3
+    W1b, W2b, dyb = W1 + g.normal(size=W1.shape) * 0.01, W2 + g.normal(size=W2.shape) * 0.01, dy * 1.1
+    ids, w = oracle.route(g.normal(size=(T, E)), k)
+    full = oracle.backward(x, W1, W2, ids, w, dy, W1_dx=W1b, W2_da=W2b, dy_da=dyb)
+    for t in range(T):
+        dxt, dwt = oracle.token_backward(x[t], W1, W2, ids[t], w[t], dy[t], W1_dx=W1b, W2_da=W2b, dy_da=dyb[t])
+        np.testing.assert_allclose(dxt, full["dx"][t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dwt, full["d_topk_w"][t], rtol=1e-12, atol=1e-12)
