@@ -58,8 +58,10 @@ struct BwdLayout {
       w1e, w2q, w2e, total;
   int max_partials;
 };
+// MXFP8 adds W1 and W2 quantised along the data gradients' K (row blocks), produced by the
+// forward's single pass over each weight matrix and read by the backward.
 struct SavedLayout {
-  size_t H, As, total;
+  size_t H, As, w1q, w1e, w2q, w2e, total;
 };
 
 FwdLayout fwd_layout(const moe_dims* d) {
@@ -148,14 +150,7 @@ BwdLayout bwd_layout(const moe_dims* d) {
     off += al256((size_t)A * 2 * ff);
     L.dHs = off;
     off += al256((size_t)A * (2 * ff / 32));
-    L.w1q = off;
-    off += al256(E * dd * 2 * ff);
-    L.w1e = off;
-    off += al256(E * dd * 2 * ff / 32);
-    L.w2q = off;
-    off += al256(E * ff * dd);
-    L.w2e = off;
-    off += al256(E * ff * dd / 32);
+    (void)E;
   }
   L.total = off;
   return L;
@@ -177,7 +172,19 @@ SavedLayout saved_layout(const moe_dims* d) {
   SavedLayout L{};
   L.H = 0;
   L.As = al256((size_t)A * 2 * d->f * 2);
-  L.total = L.As + al256((size_t)A * d->f * 2);
+  size_t off = L.As + al256((size_t)A * d->f * 2);
+  if (d->dtype == MOE_MXFP8) {
+    const size_t E = d->E, dd = d->d, ff = d->f;
+    L.w1q = off;
+    off += al256(E * dd * 2 * ff);
+    L.w1e = off;
+    off += al256(E * dd * 2 * ff / 32);
+    L.w2q = off;
+    off += al256(E * ff * dd);
+    L.w2e = off;
+    off += al256(E * ff * dd / 32);
+  }
+  L.total = off;
   return L;
 }
 
@@ -290,9 +297,13 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
     uint8_t *xq = (uint8_t*)(w + L.xq), *xe = (uint8_t*)(w + L.xe);
     uint8_t *w1q = (uint8_t*)(w + L.w1q), *w1e = (uint8_t*)(w + L.w1e);
     uint8_t *w2q = (uint8_t*)(w + L.w2q), *w2e = (uint8_t*)(w + L.w2e);
+    uint8_t *w1bq = (uint8_t*)(sv + SL.w1q), *w1be = (uint8_t*)(sv + SL.w1e);
+    uint8_t *w2bq = (uint8_t*)(sv + SL.w2q), *w2be = (uint8_t*)(sv + SL.w2e);
     MOE_TRY("mx_quant_x", launch_mx_quant((const uint16_t*)x, 1, s.T, s.d, 0, xq, xe, st));
-    MOE_TRY("mx_quant_w1", launch_mx_quant((const uint16_t*)W1, s.E, s.d, 2 * s.f, 1, w1q, w1e, st));
-    MOE_TRY("mx_quant_w2", launch_mx_quant((const uint16_t*)W2, s.E, s.f, s.d, 1, w2q, w2e, st));
+    // each weight matrix read once: blocks along the forward K (workspace) and along the data
+    // gradients' K (saved, for the backward)
+    MOE_TRY("mx_quant_w1", launch_mx_quant_dual((const uint16_t*)W1, s.E, s.d, 2 * s.f, w1q, w1e, w1bq, w1be, st));
+    MOE_TRY("mx_quant_w2", launch_mx_quant_dual((const uint16_t*)W2, s.E, s.f, s.d, w2q, w2e, w2bq, w2be, st));
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
     MOE_TRY("gemm_up", launch_mx_up(s, xq, xe, w1q, w1e, topk_w, offsets, perm, tiles, ntiles, H, As, Asq, Ase, st));
     MOE_TRY("gemm_down", launch_mx_down(s, Asq, Ase, w2q, w2e, offsets, perm, tiles, ntiles, Op, st));
@@ -369,11 +380,10 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   if (is_mx(dims)) {
     uint8_t *dyq = (uint8_t*)(w + L.dyq), *dye = (uint8_t*)(w + L.dys);
     uint8_t *dHq = (uint8_t*)(w + L.dHq), *dHe = (uint8_t*)(w + L.dHs);
-    uint8_t *w1q = (uint8_t*)(w + L.w1q), *w1e = (uint8_t*)(w + L.w1e);
-    uint8_t *w2q = (uint8_t*)(w + L.w2q), *w2e = (uint8_t*)(w + L.w2e);
+    // W1, W2 in row blocks (K = 2f and d), quantised by the forward
+    const uint8_t *w1q = (const uint8_t*)(sv + SL.w1q), *w1e = (const uint8_t*)(sv + SL.w1e);
+    const uint8_t *w2q = (const uint8_t*)(sv + SL.w2q), *w2e = (const uint8_t*)(sv + SL.w2e);
     MOE_TRY("mx_quant_dy", launch_mx_quant((const uint16_t*)dy, 1, s.T, s.d, 0, dyq, dye, st));
-    MOE_TRY("mx_quant_w2", launch_mx_quant((const uint16_t*)W2, 1, s.E * s.f, s.d, 0, w2q, w2e, st));
-    MOE_TRY("mx_quant_w1", launch_mx_quant((const uint16_t*)W1, 1, s.E * s.d, 2 * s.f, 0, w1q, w1e, st));
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
     MOE_TRY("gemm_dact", launch_mx_dact(s, dyq, dye, w2q, w2e, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq, dHe,
                                         dwp, st));

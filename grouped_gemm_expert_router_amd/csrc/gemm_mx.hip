@@ -438,6 +438,81 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
   *(u32x2*)eo = ev;
 }
 
+// Both orientations in one pass (a weight matrix read once): src bf16 [batch, rows, cols] ->
+// qc/qce in column blocks (exponents [batch, rows/32, cols]) and qr/qre in row blocks
+// (exponents [batch, rows, cols/32]).  One block of 256 threads per 32 x 256 tile: thread t owns
+// 4 rows (group t / 32) x 8 columns (chunk t % 32).  Row blocks: 4 neighbouring lanes.  Column
+// blocks: the 8 row groups' maxima meet in LDS.
+__global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __restrict__ src, int rows, int cols,
+                                                            uint8_t* __restrict__ qc, uint8_t* __restrict__ qce,
+                                                            uint8_t* __restrict__ qr, uint8_t* __restrict__ qre) {
+  __shared__ float s_amax[8][256];
+  const int t = threadIdx.x, cc = t & 31, rg = t >> 5;
+  const int tiles_c = cols / 256, tiles_r = rows / 32;
+  const int64_t b = blockIdx.x / (tiles_r * tiles_c);
+  const int rem = blockIdx.x % (tiles_r * tiles_c);
+  const int r0 = (rem / tiles_c) * 32, c0 = (rem % tiles_c) * 256 + cc * 8;
+  const int64_t mat = b * (int64_t)rows * cols;
+  float v[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 w = *(const uint4*)(src + mat + (int64_t)(r0 + 4 * rg + i) * cols + c0);
+    v[i][0] = lo_bf16(w.x); v[i][1] = hi_bf16(w.x); v[i][2] = lo_bf16(w.y); v[i][3] = hi_bf16(w.y);
+    v[i][4] = lo_bf16(w.z); v[i][5] = hi_bf16(w.z); v[i][6] = lo_bf16(w.w); v[i][7] = hi_bf16(w.w);
+  }
+  // row blocks (32 columns = 4 lanes)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t ex;
+    const u32x2 q = mx_quant8_group4(v[i], &ex);
+    const int64_t row = r0 + 4 * rg + i;
+    *(u32x2*)(qr + mat + row * cols + c0) = q;
+    if ((cc & 3) == 0) qre[(b * rows + row) * (int64_t)(cols / 32) + c0 / 32] = (uint8_t)ex;
+  }
+  // column blocks (32 rows = 8 row groups)
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(v[i][c]));
+    s_amax[rg][cc * 8 + c] = m;
+  }
+  __syncthreads();
+  float inv[8];
+  int sx[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float m = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) m = fmaxf(m, s_amax[g][cc * 8 + c]);
+    sx[c] = mx_exponent(m);
+    inv[c] = ldexpf(1.0f, -sx[c]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x2 o;
+    o.x = pack_e4m3x4(v[i][0] * inv[0], v[i][1] * inv[1], v[i][2] * inv[2], v[i][3] * inv[3]);
+    o.y = pack_e4m3x4(v[i][4] * inv[4], v[i][5] * inv[5], v[i][6] * inv[6], v[i][7] * inv[7]);
+    *(u32x2*)(qc + mat + (int64_t)(r0 + 4 * rg + i) * cols + c0) = o;
+  }
+  if (rg == 0) {
+    u32x2 ev;
+    ev.x = (uint32_t)(sx[0] + 127) | ((uint32_t)(sx[1] + 127) << 8) | ((uint32_t)(sx[2] + 127) << 16) |
+           ((uint32_t)(sx[3] + 127) << 24);
+    ev.y = (uint32_t)(sx[4] + 127) | ((uint32_t)(sx[5] + 127) << 8) | ((uint32_t)(sx[6] + 127) << 16) |
+           ((uint32_t)(sx[7] + 127) << 24);
+    *(u32x2*)(qce + (b * (rows / 32) + r0 / 32) * (int64_t)cols + c0) = ev;
+  }
+}
+
+hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, int cols, uint8_t* qc, uint8_t* qce,
+                                uint8_t* qr, uint8_t* qre, hipStream_t st) {
+  const int64_t blocks = batch * (rows / 32) * (cols / 256);
+  if (blocks == 0) return hipSuccess;
+  mx_quant_dual_kernel<<<(unsigned)blocks, 256, 0, st>>>(src, rows, cols, qc, qce, qr, qre);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int cols, int along_rows, uint8_t* q,
                            uint8_t* qe, hipStream_t st) {
   if (batch * rows * cols == 0) return hipSuccess;

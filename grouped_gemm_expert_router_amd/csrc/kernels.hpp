@@ -102,6 +102,10 @@ hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, 
 // along_rows = 1: blocks of 32 consecutive rows of a column -> exponents [batch, rows/32, cols].
 hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int cols, int along_rows, uint8_t* q,
                            uint8_t* qe, hipStream_t st);
+// Both orientations of [batch, rows, cols] in one pass (rows % 32 == 0, cols % 256 == 0):
+// column blocks into qc/qce, row blocks into qr/qre.
+hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, int cols, uint8_t* qc, uint8_t* qce,
+                                uint8_t* qr, uint8_t* qre, hipStream_t st);
 hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe, const uint8_t* W1q,
                         const uint8_t* W1e, const float* topk_w, const int32_t* offsets, const int32_t* perm,
                         const int2* tiles, const int32_t* ntiles, uint16_t* H, uint16_t* As, uint8_t* Asq,

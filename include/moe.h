@@ -52,8 +52,10 @@
  *     adatmozgatás": group-aware MXFP8 quantisation feeding an MXFP8 grouped GEMM; [TE]
  *     "צמצום הזיכרון ותקורות הכימות": one scale per 32 values).  The exponent of a block is the
  *     smallest power of two that brings its maximum magnitude within 448 (no clipping); elements
- *     round to nearest even.  The data-gradient GEMMs use weights quantised along their own K.
- *     Weight gradients are computed from bf16 operands.  d and f must be multiples of 256.
+ *     round to nearest even.  The data-gradient GEMMs use weights quantised along their own K;
+ *     moe_forward produces both quantisations in one pass over each weight matrix and keeps
+ *     the backward's in `saved`.  Weight gradients are computed from bf16 operands.  d and f
+ *     must be multiples of 256.
  *   - Alignment (MOE_ERR_ALIGN otherwise): tensors 16-byte aligned, ws and saved 256-byte
  *     aligned (every torch/hipMalloc allocation is).
  */
