@@ -133,3 +133,15 @@ def test_mx_fullsize_qwen3():
     print("[case] qwen3 MXFP8: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL_FP8}
     assert not bad, bad
+
+
+def test_mx_bitwise_determinism():
+    inp = make_inputs(200, 256, 512, 8, 4, seed=43)
+    print("[case] mx determinism", flush=True)
+    gl = GpuLayer(inp, dtype=moe.MOE_MXFP8).run()
+    first = {k: v.clone() for k, v in gl.b.items() if k not in ("ws_route", "ws_fwd", "ws_bwd")}
+    gl.run()
+    for k, v in first.items():
+        a = v.view(torch.uint8) if v.dtype != torch.uint8 else v
+        b = gl.b[k].view(torch.uint8) if gl.b[k].dtype != torch.uint8 else gl.b[k]
+        assert torch.equal(a, b), k

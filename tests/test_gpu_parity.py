@@ -34,6 +34,9 @@ CASES = {
     "one_token": (1, 128, 128, 4, 2, 11),
     "multi_tile": (300, 256, 256, 4, 2, 12),
     "wide": (200, 512, 384, 8, 4, 13),
+    # limits of the ABI: the most experts (most of them empty) and the largest k (= E)
+    "max_experts": (96, 128, 128, 1024, 4, 14),
+    "max_k": (24, 128, 128, 64, 64, 15),
 }
 
 
