@@ -475,11 +475,11 @@ def main():
     if not fp8:
         xp = torch.empty((T * k, d), dtype=torch.bfloat16, device=dev)
         pdm = moe.dims(T, d, f, E, k)  # the permute moves bf16 rows
-        moe.moe_permute(pdm, x, b["perm"], b["offsets"], xp)
+        moe.moe_permute(pdm, x, b["inv_perm"], xp)
         p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         p0.record(cur)
         for _ in range(10):
-            moe.moe_permute(pdm, x, b["perm"], b["offsets"], xp)
+            moe.moe_permute(pdm, x, b["inv_perm"], xp)
         p1.record(cur)
         torch.cuda.synchronize()
         pms = p0.elapsed_time(p1) / 10

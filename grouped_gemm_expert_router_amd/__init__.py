@@ -59,7 +59,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_plan.argtypes = [dp] + [vp] * 6 + [sz, vp]
     lib.moe_forward.argtypes = [dp] + [vp] * 13 + [sz, vp]
     lib.moe_backward.argtypes = [dp] + [vp] * 19 + [sz, vp]
-    lib.moe_permute.argtypes = [dp, vp, vp, vp, vp, vp]
+    lib.moe_permute.argtypes = [dp, vp, vp, vp, vp]
     lib.moe_combine.argtypes = [dp, vp, vp, vp, vp]
     lib.moe_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, i32, vp, vp, vp]
     lib.moe_set_stage_hook.argtypes = [STAGE_HOOK, vp]
@@ -145,8 +145,8 @@ def moe_backward(dm, dy, x, x_scale, W1, W1_scale, W2, W2_scale, topk_ids, topk_
         _ptr(dW2), _ptr(d_topk_w), _ptr(d_logits), _ptr(ws), nb, _stream(stream)))
 
 
-def moe_permute(dm, x, perm, offsets, xp, stream=None):
-    _check("moe_permute", load_library().moe_permute(ctypes.byref(dm), _ptr(x), _ptr(perm), _ptr(offsets), _ptr(xp),
+def moe_permute(dm, x, inv_perm, xp, stream=None):
+    _check("moe_permute", load_library().moe_permute(ctypes.byref(dm), _ptr(x), _ptr(inv_perm), _ptr(xp),
                                                      _stream(stream)))
 
 

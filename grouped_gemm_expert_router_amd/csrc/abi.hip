@@ -440,17 +440,16 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   return MOE_OK;
 }
 
-int moe_permute(const moe_dims* dims, const void* x, const int32_t* perm, const int32_t* offsets, void* xp,
-                void* stream) {
+int moe_permute(const moe_dims* dims, const void* x, const int32_t* inv_perm, void* xp, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
-  if (!x || !perm || !offsets || !xp) return MOE_ERR_NULL;
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !inv_perm || !xp) return MOE_ERR_NULL;
   if (!al16(x) || !al16(xp)) return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
-  MOE_TRY("permute", launch_permute((const uint16_t*)x, perm, offsets + dims->E, dims->T * dims->k, (int)dims->d,
-                                   (int)dims->k, (uint16_t*)xp, st));
-
+  MOE_TRY("permute", launch_permute((const uint16_t*)x, inv_perm, (int)dims->T, (int)dims->d, (int)dims->k,
+                                   (uint16_t*)xp, st));
   return MOE_OK;
 }
 

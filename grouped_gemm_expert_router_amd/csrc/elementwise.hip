@@ -11,22 +11,27 @@
 namespace moe {
 
 // xp[pos] = x[perm[pos] / k] for pos < *total.  One block per row, 16-byte vectors.
-__global__ __launch_bounds__(256) void permute_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-                                                      const int32_t* __restrict__ total, int d, int k,
+// Token-major: block t reads x[t] once and writes it to the sorted position of each of its
+// routed slots (inv_perm[t*k+j] >= 0), so x is read once and each copy written once.
+__global__ __launch_bounds__(256) void permute_kernel(const uint16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ inv_perm, int d, int k,
                                                       uint16_t* __restrict__ xp) {
-  const int pos = blockIdx.x;
-  if (pos >= *total) return;
-  const int t = perm[pos] / k;
+  const int t = blockIdx.x;
+  const int64_t p0 = (int64_t)t * k;
   const uint4* src = (const uint4*)(x + (size_t)t * d);
-  uint4* dst = (uint4*)(xp + (size_t)pos * d);
-  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) dst[c] = src[c];
+  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
+    const uint4 v = src[c];
+    for (int j = 0; j < k; ++j) {
+      const int pos = inv_perm[p0 + j];
+      if (pos >= 0) ((uint4*)(xp + (size_t)pos * d))[c] = v;
+    }
+  }
 }
 
-hipError_t launch_permute(const uint16_t* x, const int32_t* perm, const int32_t* offsets, int64_t A, int d, int k,
-                          uint16_t* xp, hipStream_t st) {
-  // offsets[E] holds the routed-pair count; the caller passes &offsets[E] via `offsets`.
-  if (A == 0) return hipSuccess;
-  permute_kernel<<<(unsigned)A, 256, 0, st>>>(x, perm, offsets, d, k, xp);
+hipError_t launch_permute(const uint16_t* x, const int32_t* inv_perm, int T, int d, int k, uint16_t* xp,
+                          hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  permute_kernel<<<(unsigned)T, 256, 0, st>>>(x, inv_perm, d, k, xp);
   return hipGetLastError();
 }
 

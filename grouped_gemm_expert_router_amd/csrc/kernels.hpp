@@ -122,8 +122,8 @@ hipError_t launch_mx_dx(const MoeShape& s, const uint8_t* dHq, const uint8_t* dH
                         const int32_t* ntiles, uint16_t* dXp, hipStream_t st);
 
 // data movement and router backward
-hipError_t launch_permute(const uint16_t* x, const int32_t* perm, const int32_t* offsets, int64_t A, int d, int k,
-                          uint16_t* xp, hipStream_t st);
+hipError_t launch_permute(const uint16_t* x, const int32_t* inv_perm, int T, int d, int k, uint16_t* xp,
+                          hipStream_t st);
 hipError_t launch_combine(const uint16_t* op, const int32_t* inv_perm, int T, int d, int k, uint16_t* y,
                           hipStream_t st);
 hipError_t launch_dlogits(const float* dwp, int nparts, const int32_t* inv_perm, const int32_t* ids,

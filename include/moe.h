@@ -149,13 +149,13 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                  void* dW1, void* dW2, float* d_topk_w, float* d_logits, void* ws,
                  size_t ws_bytes, void* stream);
 
-/* Dispatch on its own (bf16): xp[pos] = x[perm[pos] / k] for pos < offsets[E]; rows of xp at
- * or past offsets[E] are left untouched.  xp is bf16 [T*k, d].  ([JAX] "Csoportosított
- * mátrixszorzás és összevont adatmozgatás": dispatch sends tokens to their experts.)  The
- * forward pass does not call it (its GEMM gathers rows directly); it exists for callers that
- * want expert-sorted activations. */
-int moe_permute(const moe_dims* dims, const void* x, const int32_t* perm, const int32_t* offsets,
-                void* xp, void* stream);
+/* Dispatch on its own (bf16): for every slot with pos = inv_perm[t*k+j] >= 0, xp[pos] = x[t]
+ * (so xp[pos] = x[perm[pos] / k] for pos < offsets[E]); rows of xp at or past offsets[E] are left
+ * untouched.  Token-major: each row of x is read once and written to its k positions.  xp is
+ * bf16 [T*k, d].  ([JAX] "Csoportosított mátrixszorzás és összevont adatmozgatás": dispatch
+ * sends tokens to their experts.)  The forward pass does not call it (its GEMM gathers rows
+ * directly); it exists for callers that want expert-sorted activations. */
+int moe_permute(const moe_dims* dims, const void* x, const int32_t* inv_perm, void* xp, void* stream);
 
 /* Combine on its own (bf16): y[t] = sum over j = 0..k-1 with inv_perm[t*k+j] >= 0 of
  * op[t*k+j], summed in fp32 in ascending j and rounded once to bf16 (combine gathers the

@@ -140,7 +140,8 @@ def test_forward_backward_argument_errors(lib):
     assert bwd(ids=None) == moe.MOE_ERR_NULL               # d_logits requested without ids
     assert bwd(ws=wb - 1) == moe.MOE_ERR_WORKSPACE
     assert lib.moe_combine(ctypes.byref(dm), None, F, F, None) == moe.MOE_ERR_NULL
-    assert lib.moe_permute(ctypes.byref(dm), F, F, F, None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_permute(ctypes.byref(dm), F, F, None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_permute(ctypes.byref(dm), F + 4, F, F, None) == moe.MOE_ERR_ALIGN
     assert lib.moe_combine(ctypes.byref(dm), F + 4, F, F, None) == moe.MOE_ERR_ALIGN
 
 

@@ -134,7 +134,7 @@ def test_permute_then_combine_is_k_times_x_bitexact(k):
     b = gl.b
     A = inp.T * k
     xp = torch.empty((A, inp.d), dtype=torch.bfloat16, device="cuda")
-    moe.moe_permute(gl.dm, gl.x, b["perm"], b["offsets"], xp)
+    moe.moe_permute(gl.dm, gl.x, b["inv_perm"], xp)
     slot_rows = xp[b["inv_perm"].long()]                 # back to pair order for the combine
     y = torch.empty((inp.T, inp.d), dtype=torch.bfloat16, device="cuda")
     moe.moe_combine(gl.dm, slot_rows.contiguous(), b["inv_perm"], y)
