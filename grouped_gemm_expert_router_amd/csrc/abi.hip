@@ -40,7 +40,7 @@ bool is_mx(const moe_dims* d) { return d->dtype == MOE_MXFP8; }
 int row_tile(const moe_dims* d) { return d->dtype != MOE_BF16 ? kFp8BM : kGemmBM; }
 // d_topk_w partial sums per routed pair written by the activation-gradient GEMM
 int dact_parts(const moe_dims* d) {
-  return d->dtype != MOE_BF16 ? (int)d->f / 256 : (int)d->f / dact_bn((int)d->f);
+  return d->dtype != MOE_BF16 ? (int)d->f / 256 : dact_parts_bf16((int)d->f);
 }
 
 MoeShape shape_of(const moe_dims* d) {

@@ -98,13 +98,8 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   constexpr int DPT = QA + QB;
   static_assert(DPT * (S - 2) <= 63 && (BK == 32 || BK == 64), "vmcnt range");
 
-  // One LDS arena: S operand stages during the K loop, then the fp32 staging band of the
-  // epilogue (64 rows x BN columns, rows padded by 4 floats against bank conflicts).
-  constexpr int CPAD = BN + 4;
-  constexpr int CBAND_BYTES = 2 * 32 * CPAD * 4;
-  constexpr int ARENA = S * STAGE > CBAND_BYTES ? S * STAGE : CBAND_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[ARENA];
-  float* cband = reinterpret_cast<float*>(smem);
+  // LDS: the S operand stages of the K loop (the epilogue stores from registers).
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
   __shared__ float s_w[RAGGED_K ? 1 : BM];
   __shared__ int s_slot[RAGGED_K ? 1 : BM];
 
@@ -341,7 +336,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
 #if GEMM_SCHED
       // LDS read instructions of one step: b128 per KM fragment, two transpose reads per KN one
       if (kk + 1 < KS) sched_interleave<FM * FN, FM * (A_KN ? 2 : 1) + FN * (B_KN ? 2 : 1)>();
@@ -375,127 +370,180 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     if (it + S - 1 < nk) issue(it + S - 1, (it + S - 1) % S);
     compute(it % S);
   }
-  __syncthreads();
 
   // ------------------------------------------------------------------ epilogues
-  // Pass i stages fragment row-block i of both wave rows: band row q = 32*wm + (row in block),
-  // tile row = wm*TM + 32*i + (q % 32); band column = the LDS B row of the value (for UP:
-  // gate columns [0, BN/2), up columns [BN/2, BN)).  32x32 accumulator layout: lane holds
-  // column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4, r = 0..15.
-  const int lcol = lane & 31;
-  constexpr int CH = BN / 8;             // 8-column chunks per band row
+  // The MFMAs take the B fragment as their first operand, so each 32x32 accumulator block is
+  // held transposed: lane l holds tile row wm*TM + 32*i + l%32 and, for r = 0..15, the column
+  // b_row(j) + 8*(r/4) + 4*(l/32) + r%4.  Exchanging half-waves (v_permlane32_swap) turns the
+  // four 4-column groups of lanes l and l+32 into two runs of 8 consecutive columns each, at
+  // 8h and 16 + 8h (h = l/32), which are stored as 16-byte chunks straight from registers.
+  const int h = lane >> 5, lrow = lane & 31;
+  // bf16 of one block in that order: lo = columns 8h..8h+7, hi = columns 16+8h..23+8h
+  auto pack_rows = [&](const f32x16_t& v, uint4& lo, uint4& hi) __attribute__((always_inline)) {
+    uint32_t p[4][2];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int c = b_row(j) + lcol;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        cband[q * CPAD + c] = acc[i][j][r];
-      }
+    for (int q = 0; q < 4; ++q) {
+      p[q][0] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
+      p[q][1] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
     }
-    __syncthreads();
-    auto tile_row = [&](int q) __attribute__((always_inline)) { return (q >> 5) * TM + 32 * i + (q & 31); };
-    if constexpr (MODE == M_UP) {
-      // chunk = 8 gate columns + the matching 8 up columns of one row
-      for (int id = tid; id < 64 * (CH / 2); id += NTH) {
-        const int q = id / (CH / 2), cc = id % (CH / 2);
-        const int lr = tile_row(q);
-        if (lr < mrows) {
-          const float* gp = &cband[q * CPAD + cc * 8];
-          const float* up = &cband[q * CPAD + BN / 2 + cc * 8];
-          const float w = s_w[lr];
-          uint32_t hg[4], hu[4], as[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float g0 = gp[2 * t], g1 = gp[2 * t + 1], u0 = up[2 * t], u1 = up[2 * t + 1];
-            hg[t] = pack_bf16x2(g0, g1);
-            hu[t] = pack_bf16x2(u0, u1);
-            as[t] = pack_bf16x2(w * g0 * sigmoidf_fast(g0) * u0, w * g1 * sigmoidf_fast(g1) * u1);
-          }
-          const int64_t pos = m0 + lr;
-          const int col = n0 + cc * 8;
-          *(uint4*)&g.C0[pos * g.ldc0 + col] = make_uint4(hg[0], hg[1], hg[2], hg[3]);
-          *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(hu[0], hu[1], hu[2], hu[3]);
-          *(uint4*)&g.C1[pos * g.ldc1 + col] = make_uint4(as[0], as[1], as[2], as[3]);
+    for (int a = 0; a < 4; a += 2)
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(p[a][d], p[a + 1][d], false, false);
+        p[a][d] = r[0];
+        p[a + 1][d] = r[1];
+      }
+    lo = make_uint4(p[0][0], p[0][1], p[1][0], p[1][1]);
+    hi = make_uint4(p[2][0], p[2][1], p[3][0], p[3][1]);
+  };
+
+  if constexpr (MODE == M_UP) {
+    // gate block j and up block j + FN/2 hold the same columns of the same rows
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int lr = wm * TM + 32 * i + lrow;
+      const bool ok = lr < mrows;
+      const float w = s_w[lr];
+      const int64_t pos = m0 + lr;
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+        const f32x16_t& G = acc[i][j];
+        const f32x16_t& U = acc[i][j + FN / 2];
+        f32x16_t a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = w * G[r] * sigmoidf_fast(G[r]) * U[r];
+        uint4 glo, ghi, ulo, uhi, alo, ahi;
+        pack_rows(G, glo, ghi);
+        pack_rows(U, ulo, uhi);
+        pack_rows(a, alo, ahi);
+        if (ok) {
+          const int col = n0 + wn * (TN / 2) + 32 * j + 8 * h;
+          uint16_t* hrow = g.C0 + pos * g.ldc0;
+          uint16_t* arow = g.C1 + pos * g.ldc1;
+          *(uint4*)(hrow + col) = glo;
+          *(uint4*)(hrow + col + 16) = ghi;
+          *(uint4*)(hrow + g.f + col) = ulo;
+          *(uint4*)(hrow + g.f + col + 16) = uhi;
+          *(uint4*)(arow + col) = alo;
+          *(uint4*)(arow + col + 16) = ahi;
         }
       }
-    } else if constexpr (MODE == M_DACT) {
-      // G = dL/dAs.  a = silu(g) u from the saved H; d_topk_w partial = <G, a> over this
-      // tile's columns; da = w G; dH = [da u sig(g) (1 + g (1 - sig(g))), da silu(g)].
-      // A row's CH chunks sit in CH consecutive lanes (CH = 32 or 16), summed by a fixed
-      // butterfly; chunk 0's lane writes the row's partial.
-      static_assert(CH == 32 || CH == 16, "row chunks must map onto one half-wave");
-      for (int id = tid; id < 64 * CH; id += NTH) {
-        const int q = id / CH, cc = id % CH;
-        const int lr = tile_row(q);
-        const bool ok = lr < mrows;
-        float part = 0.0f;
-        if (ok) {
-          const int64_t pos = m0 + lr;
-          const int col = n0 + cc * 8;
-          const uint4 hg = *(const uint4*)&g.Hs[pos * g.ldh + col];
-          const uint4 hu = *(const uint4*)&g.Hs[pos * g.ldh + g.f + col];
-          const float* Gp = &cband[q * CPAD + cc * 8];
-          const float w = s_w[lr];
+    }
+  } else if constexpr (MODE == M_DACT) {
+    static_assert(WN == 4, "the d_topk_w part count assumes 4 waves across N");
+    // G = dL/dAs.  a = silu(g) u from the saved H; da = w G; dH = [da u sig(g) (1 + g (1 - sig(g))),
+    // da silu(g)]; the d_topk_w partial <G, a> of a row over this wave's columns goes to part
+    // nt * WN + wn.  The H of block (i+1, j) is loaded as soon as block (i, j) is done with its
+    // registers, so the loads overlap the remaining blocks' arithmetic.
+    uint4 hg[FN][2], hu[FN][2];
+    auto load_h = [&](int i, int j) __attribute__((always_inline)) {
+      const int lr = wm * TM + 32 * i + lrow;
+      const int64_t pos = m0 + (lr < mrows ? lr : 0);
+      const uint16_t* hrow = g.Hs + pos * g.ldh + n0 + b_row(j) + 8 * h;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        hg[j][c] = *(const uint4*)(hrow + 16 * c);
+        hu[j][c] = *(const uint4*)(hrow + g.f + 16 * c);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < FN; ++j) load_h(0, j);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int lr = wm * TM + 32 * i + lrow;
+      const bool ok = lr < mrows;
+      const float w = s_w[lr];
+      const int64_t pos = m0 + lr;
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        // fp32 half-wave exchange (in place: the block is dead afterwards): then G[8c + e] is
+        // column 16c + 8h + e
+        f32x16_t& G = acc[i][j];
+#pragma unroll
+        for (int a = 0; a < 16; a += 8)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(G[a + t]), __float_as_uint(G[a + 4 + t]),
+                                                             false, false);
+            G[a + t] = __uint_as_float(r[0]);
+            G[a + 4 + t] = __uint_as_float(r[1]);
+          }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
           uint32_t dg[4], du[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const uint32_t wg = word_of(hg, t), wu = word_of(hu, t);
+            const uint32_t wg = word_of(hg[j][c], t), wu = word_of(hu[j][c], t);
             float r0, r1, s0, s1;
             {
-              const float gv = lo_bf16(wg), uv = lo_bf16(wu), G = Gp[2 * t];
-              const float sg = sigmoidf_fast(gv), sl = gv * sg, da = w * G;
-              part += G * (sl * uv);
+              const float gv = lo_bf16(wg), uv = lo_bf16(wu), Gv = G[8 * c + 2 * t];
+              const float sg = sigmoidf_fast(gv), sl = gv * sg, da = w * Gv;
+              part += Gv * (sl * uv);
               r0 = da * uv * sg * (1.0f + gv * (1.0f - sg));
               s0 = da * sl;
             }
             {
-              const float gv = hi_bf16(wg), uv = hi_bf16(wu), G = Gp[2 * t + 1];
-              const float sg = sigmoidf_fast(gv), sl = gv * sg, da = w * G;
-              part += G * (sl * uv);
+              const float gv = hi_bf16(wg), uv = hi_bf16(wu), Gv = G[8 * c + 2 * t + 1];
+              const float sg = sigmoidf_fast(gv), sl = gv * sg, da = w * Gv;
+              part += Gv * (sl * uv);
               r1 = da * uv * sg * (1.0f + gv * (1.0f - sg));
               s1 = da * sl;
             }
             dg[t] = pack_bf16x2(r0, r1);
             du[t] = pack_bf16x2(s0, s1);
           }
-          *(uint4*)&g.C0[pos * g.ldc0 + col] = make_uint4(dg[0], dg[1], dg[2], dg[3]);
-          *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(du[0], du[1], du[2], du[3]);
+          if (ok) {
+            uint16_t* drow = g.C0 + pos * g.ldc0 + n0 + b_row(j) + 8 * h + 16 * c;
+            *(uint4*)drow = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+            *(uint4*)(drow + g.f) = make_uint4(du[0], du[1], du[2], du[3]);
+          }
         }
+        if (i + 1 < FM) load_h(i + 1, j);
+      }
+      part += __shfl_xor(part, 32, 64);  // lanes l and l+32 hold the same row
+      if (ok && h == 0) g.dwp[pos * g.nparts + nt * WN + wn] = part;
+    }
+  } else if (RAGGED_K && pslot >= 0) {
+    // one chunk of a split expert: fp32 partial, summed later in chunk order; each 4-column
+    // group is one 16-byte store
+    float* out = g.partial + (int64_t)(pslot + kchunk) * g.Mo * g.N;
 #pragma unroll
-        for (int m = CH / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-        if (ok && cc == 0) g.dwp[(int64_t)(m0 + lr) * g.nparts + nt] = part;
+    for (int i = 0; i < FM; ++i) {
+      float* orow = out + (int64_t)(m0 + wm * TM + 32 * i + lrow) * g.N + n0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(orow + b_row(j) + 8 * q + 4 * h) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
+  } else {
+    // plain bf16 store: DOWN/DX rows go to the pair's slot, weight-gradient rows to dW[e]
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int lr = wm * TM + 32 * i + lrow;
+      bool ok;
+      int64_t orow;
+      if constexpr (RAGGED_K) {
+        ok = true;
+        orow = (int64_t)e * g.Mo + m0 + lr;
+      } else {
+        ok = lr < mrows;
+        orow = s_slot[lr];
       }
-    } else if (RAGGED_K && pslot >= 0) {
-      // one chunk of a split expert: fp32 partial, summed later in chunk order
-      float* out = g.partial + (int64_t)(pslot + kchunk) * g.Mo * g.N;
-      for (int id = tid; id < 64 * CH; id += NTH) {
-        const int q = id / CH, cc = id % CH;
-        const int lr = tile_row(q);
-        const float* cp = &cband[q * CPAD + cc * 8];
-        float* o = out + (int64_t)(m0 + lr) * g.N + n0 + cc * 8;
-        *(float4*)o = make_float4(cp[0], cp[1], cp[2], cp[3]);
-        *(float4*)(o + 4) = make_float4(cp[4], cp[5], cp[6], cp[7]);
-      }
-    } else {
-      // plain bf16 store: DOWN/DX rows go to the pair's slot, WG rows to dW[e]
-      for (int id = tid; id < 64 * CH; id += NTH) {
-        const int q = id / CH, cc = id % CH;
-        const int lr = tile_row(q);
-        if (lr < mrows) {
-          const float* cp = &cband[q * CPAD + cc * 8];
-          const uint4 o = make_uint4(pack_bf16x2(cp[0], cp[1]), pack_bf16x2(cp[2], cp[3]),
-                                     pack_bf16x2(cp[4], cp[5]), pack_bf16x2(cp[6], cp[7]));
-          int64_t orow;
-          if constexpr (RAGGED_K) orow = (int64_t)e * g.Mo + m0 + lr;
-          else orow = s_slot[lr];
-          *(uint4*)&g.C0[orow * g.ldc0 + n0 + cc * 8] = o;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        uint4 lo, hi;
+        pack_rows(acc[i][j], lo, hi);
+        if (ok) {
+          uint16_t* dst = g.C0 + orow * g.ldc0 + n0 + b_row(j) + 8 * h;
+          *(uint4*)dst = lo;
+          *(uint4*)(dst + 16) = hi;
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -520,8 +568,8 @@ hipError_t run(const GemmArgs& g, int bm, int bn, dim3 grid, hipStream_t st) {
     grouped_gemm_kernel<MODE, 256, 128, (MODE == M_UP ? 2 : 4), 1, BKC><<<grid, (MODE == M_UP ? 256 : 512), 0, st>>>(g);
   else if ((MODE == M_WG || MODE == M_WG1) && bm == 128 && bn == 256)
     grouped_gemm_kernel<MODE, 128, 256, 4, 1, BKC><<<grid, 512, 0, st>>>(g);
-  else if (bm == 128 && bn == 128)
-    grouped_gemm_kernel<MODE, 128, 128, 2, 2, 32><<<grid, 256, 0, st>>>(g);
+  else if (MODE != M_DACT && bm == 128 && bn == 128)
+    grouped_gemm_kernel<MODE == M_DACT ? M_DOWN : MODE, 128, 128, 2, 2, 32><<<grid, 256, 0, st>>>(g);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -543,6 +591,9 @@ GemmArgs base_args(const MoeShape& s, const int32_t* offsets, const int32_t* per
 }  // namespace
 
 int dact_bn(int f) { return pick_bn(f); }
+// d_topk_w partials per pair: one per (N tile, wave column); the 256 x BN tiles of the
+// activation-gradient GEMM run 4 waves across N
+int dact_parts_bf16(int f) { return (f / dact_bn(f)) * 4; }
 
 int max_row_tiles(int64_t A, int E, int bm) {
   const int64_t t = (A + bm - 1) / bm + (A < E ? A : E);
@@ -610,7 +661,7 @@ hipError_t launch_gemm_dact(const MoeShape& s, const uint16_t* dy, const uint16_
   g.ldc0 = 2 * (int64_t)s.f;
   g.dwp = dwp;
   const int bn = dact_bn(s.f);
-  g.nparts = s.f / bn;
+  g.nparts = dact_parts_bf16(s.f);
   const int64_t A = (int64_t)s.T * s.k;
   dim3 grid((unsigned)(max_row_tiles(A, s.E, kGemmBM) * (s.f / bn)));
   return run<M_DACT>(g, kGemmBM, bn, grid, st);

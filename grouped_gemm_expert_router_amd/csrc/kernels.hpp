@@ -23,6 +23,7 @@ constexpr int kGemmBM = 256;
 // Column-tile width of the activation-gradient GEMM for expert FFN dim f; f / dact_bn(f)
 // partial sums of d_topk_w are written per routed pair.
 int dact_bn(int f);
+int dact_parts_bf16(int f);
 
 int max_row_tiles(int64_t A, int E, int BM);
 
