@@ -113,3 +113,13 @@ def mx_dequantize(codes: np.ndarray, scales: np.ndarray, axis: int) -> np.ndarra
     sc = np.moveaxis(e8m0_to_f64(scales), axis, -1)
     out = c.reshape(*c.shape[:-1], c.shape[-1] // 32, 32) * sc[..., None]
     return np.moveaxis(out.reshape(c.shape), -1, axis)
+
+
+def mx_roundtrip_rows(v: np.ndarray) -> np.ndarray:
+    """MX round trip of a matrix in blocks of 32 consecutive rows (axis 0), in fp64.  A last
+    partial block is completed with zero rows, which leave its largest magnitude -- and so its
+    exponent -- unchanged; the padding is dropped from the result."""
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[0]
+    vp = np.concatenate([v, np.zeros(((-n) % 32,) + v.shape[1:])], axis=0)
+    return mx_dequantize(*mx_quantize(vp, 0), 0)[:n]

@@ -136,7 +136,7 @@ def forward(x, W1, W2, ids, w, E=None, return_saved=False):
 
 
 # ------------------------------------------------------------------------------ backward
-def backward(x, W1, W2, ids, w, dy, logits_routed=True, W1_dx=None, W2_da=None, dy_da=None, x_dw=None):
+def backward(x, W1, W2, ids, w, dy, logits_routed=True, W1_dx=None, W2_da=None, dy_da=None, x_dw=None, q_dw=None):
     """Gradients of L = sum(dy * y) for the forward above.
 
     Returns dict with dx [T,d], dW1 [E,d,2f], dW2 [E,f,d], d_topk_w [T,k] (0 on unrouted
@@ -146,7 +146,13 @@ def backward(x, W1, W2, ids, w, dy, logits_routed=True, W1_dx=None, W2_da=None, 
     The optional operands name a different copy of a tensor for one product, as a quantised
     layer has when each GEMM quantises along its own K (MXFP8): dy_da and W2_da for
     da = (w dy) W2^T and the routing-weight gradient, W1_dx for dx = dH W1^T, x_dw for
-    dW1 = x^T dH.  Left as None they are dy, W2, W1 and x."""
+    dW1 = x^T dH.  Left as None they are dy, W2, W1 and x.
+
+    q_dw, when given, is applied to each operand of the two weight-gradient products, one expert
+    at a time with its rows in the expert's sorted order: dW2[e] = q(As_e)^T q(dy_e) with
+    As_e = w * a (the routing-scaled activation the down projection consumes) and dW1[e] =
+    q(x_e)^T q(dH_e).  A layer that quantises those operands along the token axis, in blocks
+    that stay inside one expert, is modelled by q_dw = mx_roundtrip_rows."""
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
     W1_dx = W1 if W1_dx is None else W1_dx
@@ -175,12 +181,15 @@ def backward(x, W1, W2, ids, w, dy, logits_routed=True, W1_dx=None, W2_da=None, 
         a = S * U
         dYa = dy_da[R]
         dw[P] = np.sum(dYa * (a @ W2_da[e]), axis=1)   # y is linear in each routing weight
-        dW2[e] = a.T @ (wf[P][:, None] * dy[R])
+        if q_dw is None:
+            dW2[e] = a.T @ (wf[P][:, None] * dy[R])
+        else:
+            dW2[e] = q_dw(wf[P][:, None] * a).T @ q_dw(dy[R])
         da = (wf[P][:, None] * dYa) @ W2_da[e].T
         dG = da * U * sg * (1.0 + G * (1.0 - sg))      # d silu / dg = sig * (1 + g (1 - sig))
         dU = da * S
         dH = np.concatenate([dG, dU], axis=1)
-        dW1[e] = x_dw[R].T @ dH
+        dW1[e] = x_dw[R].T @ dH if q_dw is None else q_dw(x_dw[R]).T @ q_dw(dH)
         np.add.at(dx, R, dH @ W1_dx[e].T)
     out = dict(dx=dx, dW1=dW1, dW2=dW2, d_topk_w=dw.reshape(T, k), plan=pl)
     if logits_routed:
@@ -264,6 +273,22 @@ def weight_grad_entries(x, W1, W2, ids, w, dy, e, rows_i, cols_j, which):
             dh = da * u * sg * (1.0 + g * (1.0 - sg)) if j < f else da * g * sg
             out[n] = np.sum(Xe[:, i] * dh)
     return out
+
+
+def expert_weight_grads(x, W1, W2, ids, w, dy, e, W2_da=None, dy_da=None, x_dw=None, q_dw=None):
+    """(dW1[e], dW2[e]) of backward() for one expert, from that expert's rows only (same
+    arguments; the full-size checks use it where the whole backward would not fit)."""
+    k = ids.shape[1]
+    E = W1.shape[0]
+    sel = np.asarray(ids) == e
+    toks = np.flatnonzero(sel.any(axis=1))
+    sub_ids = np.where(sel[toks], 0, -1)             # the expert becomes expert 0 of a 1-expert layer
+    pick = lambda v: None if v is None else np.asarray(v, np.float64)[toks]
+    one = lambda Wt: None if Wt is None else np.asarray(Wt[e], np.float64)[None]
+    sub_w = np.where(sel[toks], np.asarray(w, np.float64)[toks], 0.0)
+    out = backward(pick(x), one(W1), one(W2), sub_ids, sub_w, pick(dy), logits_routed=False,
+                   W2_da=one(W2_da), dy_da=pick(dy_da), x_dw=pick(x_dw), q_dw=q_dw)
+    return out["dW1"][0], out["dW2"][0]
 
 
 def d_logits_from_dw(w, dw, ids, E):

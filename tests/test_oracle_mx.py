@@ -160,3 +160,79 @@ def test_token_backward_with_copies_matches_full_backward():
         dxt, dwt = oracle.token_backward(x[t], W1, W2, ids[t], w[t], dy[t], W1_dx=W1b, W2_da=W2b, dy_da=dyb[t])
         np.testing.assert_allclose(dxt, full["dx"][t], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dwt, full["d_topk_w"][t], rtol=1e-12, atol=1e-12)
+
+
+def _brute_roundtrip_rows(v):
+    """Row-block MX round trip by brute force: zero rows complete the last block of 32, each
+    column's block is quantised by _brute_force_quantize, then decoded by hand."""
+    n = v.shape[0]
+    vp = np.concatenate([v, np.zeros(((-n) % 32, v.shape[1]))])
+    codes, scales = _brute_force_quantize(vp.T.copy())           # blocks along the (padded) rows
+    val = oracle.e4m3_to_f64(codes) * np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)
+    return val.T[:n]
+
+
+def test_mx_roundtrip_rows_matches_brute_force():
+    g = np.random.default_rng(7)
+    v = g.normal(0, 1, (70, 5)) * np.exp2(g.integers(-5, 5, (1, 5)))  # two full blocks and one of 6 rows
+    v[32:64, 2] = 0.0                                                 # an all-zero block
+    np.testing.assert_array_equal(oracle.mx_roundtrip_rows(v), _brute_roundtrip_rows(v))
+    # the zero padding never decides anything: more zero rows give the same real rows
+    more = np.concatenate([v, np.zeros((30, 5))])
+    np.testing.assert_array_equal(oracle.mx_roundtrip_rows(more)[:70], oracle.mx_roundtrip_rows(v))
+
+
+def _tiny_layer(seed, T=90, d=8, f=6, E=3, k=1):
+    g = np.random.default_rng(seed)
+    x, dy = g.normal(size=(T, d)), g.normal(size=(T, d))
+    W1, W2 = g.normal(size=(E, d, 2 * f)) / 3, g.normal(size=(E, f, d)) / 3
+    L = g.normal(size=(T, E)) + np.array([1.5, 0.0, -0.5])[:E]    # expert 0 gets more than 32 rows
+    ids, w = oracle.route(L, k)
+    return x, dy, W1, W2, ids, w
+
+
+def test_backward_q_dw_identity_and_scaling():
+    x, dy, W1, W2, ids, w = _tiny_layer(8, k=2)
+    base = oracle.backward(x, W1, W2, ids, w, dy)
+    same = oracle.backward(x, W1, W2, ids, w, dy, q_dw=lambda v: v)
+    for key in ("dW1", "dW2"):                       # As^T dy = a^T (w dy): only the grouping moves
+        np.testing.assert_allclose(same[key], base[key], rtol=1e-12, atol=1e-12)
+    dbl = oracle.backward(x, W1, W2, ids, w, dy, q_dw=lambda v: 2.0 * v)
+    for key in ("dW1", "dW2"):                       # both operands of each product pass through q
+        np.testing.assert_allclose(dbl[key], 4.0 * base[key], rtol=1e-12, atol=1e-12)
+    for key in ("dx", "d_topk_w", "d_logits"):
+        np.testing.assert_array_equal(dbl[key], base[key])
+
+
+def test_backward_q_dw_one_expert_by_hand():
+    """dW2[e] and dW1[e] with row-block MX operands, rebuilt from per-row loops and the brute-force
+    quantiser, in the expert's token order."""
+    x, dy, W1, W2, ids, w = _tiny_layer(9)
+    f = W2.shape[1]
+    out = oracle.backward(x, W1, W2, ids, w, dy, q_dw=oracle.mx_roundtrip_rows)
+    for e in range(W1.shape[0]):
+        rows = [t for t in range(x.shape[0]) if ids[t, 0] == e]          # k = 1: slot 0, token order
+        assert rows, e
+        As, dH = [], []
+        for t in rows:
+            h = x[t] @ W1[e]
+            gt, ut = h[:f], h[f:]
+            sg = 1.0 / (1.0 + np.exp(-gt))
+            As.append(w[t, 0] * gt * sg * ut)
+            da = w[t, 0] * (W2[e] @ dy[t])
+            dH.append(np.concatenate([da * ut * sg * (1.0 + gt * (1.0 - sg)), da * gt * sg]))
+        As, dH = np.array(As), np.array(dH)
+        q = _brute_roundtrip_rows
+        np.testing.assert_allclose(out["dW2"][e], q(As).T @ q(dy[rows]), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out["dW1"][e], q(x[rows]).T @ q(dH), rtol=1e-12, atol=1e-12)
+    assert max(sum(ids[:, 0] == e) for e in range(3)) > 32          # a block boundary was crossed
+
+
+def test_expert_weight_grads_matches_backward():
+    x, dy, W1, W2, ids, w = _tiny_layer(10, k=2)
+    for q in (None, oracle.mx_roundtrip_rows):
+        full = oracle.backward(x, W1, W2, ids, w, dy, q_dw=q)
+        for e in range(W1.shape[0]):
+            dW1, dW2 = oracle.expert_weight_grads(x, W1, W2, ids, w, dy, e, q_dw=q)
+            np.testing.assert_allclose(dW1, full["dW1"][e], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(dW2, full["dW2"][e], rtol=1e-12, atol=1e-12)
