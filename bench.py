@@ -72,7 +72,10 @@ def log(*a):
 
 STAGE_KERNEL_MX = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_mx_kernel<0>",
                        gemm_down="moe::grouped_gemm_mx_kernel<1>", gemm_dact="moe::grouped_gemm_mx_kernel<2>",
-                       gemm_dx="moe::grouped_gemm_mx_kernel<3>", mx_quant="moe::mx_quant_")
+                       gemm_dx="moe::grouped_gemm_mx_kernel<3>", gemm_dw2="moe::grouped_gemm_mx_wg_kernel<0>",
+                       gemm_dw1="moe::grouped_gemm_mx_wg_kernel<1>", mx_quant_t="moe::mx_quant_tokens",
+                       mx_pad="moe::mx_pad_offsets", mx_quant="moe::mx_quant_")
+MX_FP8_STAGES = FP8_STAGES + ("gemm_dw2", "gemm_dw1")
 
 
 def is_fp8(config):
@@ -81,6 +84,8 @@ def is_fp8(config):
 
 
 def stage_dtype(config, stage):
+    if config.endswith(":mxfp8"):      # every GEMM, weight gradients included, runs MXFP8
+        return "fp8" if stage in MX_FP8_STAGES else "bf16"
     return "fp8" if (is_fp8(config) and stage in FP8_STAGES) else "bf16"
 
 
@@ -107,6 +112,12 @@ def stage_bytes(stage, T, d, f, E, k, A):
         return T * d + T * (d // 128) * 4 + T * d * 2
     if stage in ("mx_quant_x", "mx_quant_dy"):
         return T * d * 2 + T * d + T * d // 32
+    if stage == "mx_quant_as_t":                            # sorted rows in, token-axis blocks out
+        return A * f * 2 + A * f + A * f // 32
+    if stage == "mx_quant_dh_t":
+        return A * 2 * f * 2 + A * 2 * f + A * 2 * f // 32
+    if stage in ("mx_quant_x_t", "mx_quant_dy_t"):           # each token row read once, A rows out
+        return T * d * 2 + A * d + A * d // 32
     if stage in ("mx_quant_w1", "mx_quant_w2"):
         return E * d * f * (2 + 1) + E * d * f // 32     # one of W1 (2df) / W2 (df): bytes of W1 halved
     return None

@@ -49,13 +49,15 @@ MoeShape shape_of(const moe_dims* d) {
 
 // fp8: asq/ass (As in e4m3 + scales); dyq/dys, dHq/dHs, xb (x dequantised to bf16).
 // MXFP8 (codes + E8M0 exponents): asq/ass; xq/xe, w1q/w1e and w2q/w2e (forward quantisation of
-// x, W1 and W2); dyq/dys, dHq/dHs, w1q/w1e and w2q/w2e (W1, W2 along the data gradients' K).
+// x, W1 and W2); dyq/dys, dHq/dHs, w1q/w1e and w2q/w2e (W1, W2 along the data gradients' K);
+// for the weight gradients poff (padded expert offsets) and tqa/tea, tqb/teb (the two operands
+// of one product quantised along the token axis, reused by dW2 and then dW1).
 struct FwdLayout {
   size_t tiles, ntiles, op, asq, ass, xq, xe, w1q, w1e, w2q, w2e, total;
 };
 struct BwdLayout {
   size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dHq, dHs, xb, w1q,
-      w1e, w2q, w2e, total;
+      w1e, w2q, w2e, poff, tqa, tea, tqb, teb, total;
   int max_partials;
 };
 // MXFP8 adds W1 and W2 quantised along the data gradients' K (row blocks), produced by the
@@ -150,7 +152,18 @@ BwdLayout bwd_layout(const moe_dims* d) {
     off += al256((size_t)A * 2 * ff);
     L.dHs = off;
     off += al256((size_t)A * (2 * ff / 32));
-    (void)E;
+    const size_t P = (size_t)mx_padded_rows(A, (int)E);
+    const size_t ca = ff > dd ? ff : dd, cb = dd > 2 * ff ? dd : 2 * ff;  // As or x; dy or dH
+    L.poff = off;
+    off += al256((E + 1) * sizeof(int32_t));
+    L.tqa = off;
+    off += al256(P * ca);
+    L.tea = off;
+    off += al256(P / 32 * ca);
+    L.tqb = off;
+    off += al256(P * cb);
+    L.teb = off;
+    off += al256(P / 32 * cb);
   }
   L.total = off;
   return L;
@@ -389,12 +402,21 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                                         dwp, st));
     MOE_TRY("gemm_dx", launch_mx_dx(s, dHq, dHe, w1q, w1e, offsets, perm, tiles, ntiles, dXp, st));
     MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
-    MOE_TRY("tokrow", launch_tokrow(perm, offsets, s.E, (int64_t)s.T * s.k, s.k, tokrow, st));
-    MOE_TRY("wg_split", launch_wg_split(s, offsets, sp, st));
-    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, sp, (uint16_t*)dW2, st));
-    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.f * s.d, (uint16_t*)dW2, st));
-    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, (const uint16_t*)x, dH, offsets, perm, tokrow, sp, (uint16_t*)dW1, st));
-    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.d * 2 * s.f, (uint16_t*)dW1, st));
+    // weight gradients: both operands in token-axis blocks inside each expert's padded segment
+    int32_t* poff = (int32_t*)(w + L.poff);
+    uint8_t *tqa = (uint8_t*)(w + L.tqa), *tea = (uint8_t*)(w + L.tea);
+    uint8_t *tqb = (uint8_t*)(w + L.tqb), *teb = (uint8_t*)(w + L.teb);
+    const WgSplit spm = wg_split_of(L, w, poff);
+    MOE_TRY("mx_pad", launch_mx_pad_offsets(offsets, s.E, poff, st));
+    MOE_TRY("wg_split", launch_wg_split(s, poff, spm, st));
+    MOE_TRY("mx_quant_as_t", launch_mx_quant_tokens(As, s.f, 0, s, offsets, perm, poff, tqa, tea, st));
+    MOE_TRY("mx_quant_dy_t", launch_mx_quant_tokens((const uint16_t*)dy, s.d, 1, s, offsets, perm, poff, tqb, teb, st));
+    MOE_TRY("gemm_dw2", launch_mx_wg(0, s, tqa, tea, s.f, tqb, teb, s.d, poff, spm, (uint16_t*)dW2, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, spm, (int64_t)s.f * s.d, (uint16_t*)dW2, st));
+    MOE_TRY("mx_quant_x_t", launch_mx_quant_tokens((const uint16_t*)x, s.d, 1, s, offsets, perm, poff, tqa, tea, st));
+    MOE_TRY("mx_quant_dh_t", launch_mx_quant_tokens(dH, 2 * s.f, 0, s, offsets, perm, poff, tqb, teb, st));
+    MOE_TRY("gemm_dw1", launch_mx_wg(1, s, tqa, tea, s.d, tqb, teb, 2 * s.f, poff, spm, (uint16_t*)dW1, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, spm, (int64_t)s.d * 2 * s.f, (uint16_t*)dW1, st));
     MOE_TRY("dlogits", launch_dlogits(dwp, dact_parts(dims), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w,
                                       d_logits, st));
     return MOE_OK;

@@ -652,4 +652,332 @@ hipError_t launch_mx_dx(const MoeShape& s, const uint8_t* dHq, const uint8_t* dH
   return run_mx<X_DX>(g, (int64_t)s.T * s.k, s.E, s.d / 256, st);
 }
 
+
+// ---------------------------------------------------------------------- weight gradients
+// dW2[e] = As_e^T dy_e and dW1[e] = x_e^T dH_e, with K = the expert's rows (ragged K).  Both
+// operands are quantised along that K in blocks of 32 rows that stay inside one expert (the
+// pages' MXFP8 with group-aware quantisation: JAX MoE page, section "Csoportosított
+// mátrixszorzás és összevont adatmozgatás").  Each expert's rows go to a segment of a padded
+// buffer that starts at poff[e], a multiple of 128, and is completed with zero rows: a zero row
+// leaves a block's maximum unchanged and adds nothing to a product, and no 128-deep K step of
+// the GEMM below ever mixes two experts.
+
+// poff[e] = sum over e' < e of count(e') rounded up to 128; poff[E] = the padded total.
+__global__ __launch_bounds__(1024) void mx_pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
+                                                             int32_t* __restrict__ poff) {
+  __shared__ int sh[64];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int ex;
+  const int tot = block_excl_scan_1024((c + 127) & ~127, sh, &ex);
+  if (e < E) poff[e] = ex;
+  if (e == 0) poff[E] = tot;
+}
+
+// Rows of a bf16 source [*, C] in the experts' sorted order -- row perm[pos] / kslots of a
+// token-major source when gather, else row pos -- quantised along the rows into the padded
+// segments: codes [P, C], exponents [P / 32, C].  One block per 32 padded rows and 2048
+// columns; thread t owns 8 columns: a first pass over the 32 rows finds their maxima, a second
+// (from L2) writes the codes.  Rows past the expert's count are zero.
+__global__ __launch_bounds__(256) void mx_quant_tokens_kernel(const uint16_t* __restrict__ src, int C, int gather,
+                                                              int kslots, const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ perm,
+                                                              const int32_t* __restrict__ poff, int E,
+                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ qe) {
+  __shared__ int64_t s_row[32];
+  const int pp0 = blockIdx.x * 32;
+  if (pp0 >= poff[E]) return;                        // block-uniform: past the padded total
+  if (threadIdx.x < 32) {
+    // the expert whose segment holds pp0: poff[lo] <= pp0 < poff[hi] throughout
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (poff[mid] <= pp0) lo = mid;
+      else hi = mid;
+    }
+    const int local = pp0 - poff[lo] + (int)threadIdx.x;
+    int64_t row = -1;
+    if (local < offsets[lo + 1] - offsets[lo]) {
+      const int pos = offsets[lo] + local;
+      row = gather ? (int64_t)(perm[pos] / kslots) : (int64_t)pos;
+    }
+    s_row[threadIdx.x] = row;
+  }
+  __syncthreads();
+  const int c0 = blockIdx.y * 2048 + threadIdx.x * 8;
+  if (c0 >= C) return;                               // C is a multiple of 8
+  auto load8 = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
+    const int64_t row = s_row[r];
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (row >= 0) w = *(const uint4*)(src + row * C + c0);
+    v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x); v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
+    v[4] = lo_bf16(w.z); v[5] = hi_bf16(w.z); v[6] = lo_bf16(w.w); v[7] = hi_bf16(w.w);
+  };
+  float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) {
+    float v[8];
+    load8(r, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) amax[t] = fmaxf(amax[t], fabsf(v[t]));
+  }
+  int sx[8];
+  float inv[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    sx[t] = mx_exponent(amax[t]);
+    inv[t] = ldexpf(1.0f, -sx[t]);  // exact: a power of two
+  }
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) {
+    float v[8];
+    load8(r, v);
+    u32x2 o;
+    o.x = pack_e4m3x4(v[0] * inv[0], v[1] * inv[1], v[2] * inv[2], v[3] * inv[3]);
+    o.y = pack_e4m3x4(v[4] * inv[4], v[5] * inv[5], v[6] * inv[6], v[7] * inv[7]);
+    *(u32x2*)(q + (int64_t)(pp0 + r) * C + c0) = o;
+  }
+  u32x2 ev;
+  ev.x = (uint32_t)(sx[0] + 127) | ((uint32_t)(sx[1] + 127) << 8) | ((uint32_t)(sx[2] + 127) << 16) |
+         ((uint32_t)(sx[3] + 127) << 24);
+  ev.y = (uint32_t)(sx[4] + 127) | ((uint32_t)(sx[5] + 127) << 8) | ((uint32_t)(sx[6] + 127) << 16) |
+         ((uint32_t)(sx[7] + 127) << 24);
+  *(u32x2*)(qe + (int64_t)(pp0 / 32) * C + c0) = ev;
+}
+
+struct MxWgArgs {
+  const uint8_t* A;   // codes [P, Mo]: the product's left operand, k-major (row = padded position)
+  const uint8_t* Ae;  // exponents [P / 32, Mo]
+  const uint8_t* B;   // codes [P, N]
+  const uint8_t* Be;  // exponents [P / 32, N]
+  int Mo, N;
+  const int32_t* poff;
+  const int2* units;     // (expert, chunk) work units, largest first
+  const int32_t* meta;   // [0] units, [1] chunk rows KC, [2] 1 = bucketed XCD order
+  const int32_t* pslot;  // first fp32 partial of a split expert, -1 if not split
+  float* partial;
+  uint16_t* dW;          // [E, Mo, N] bf16
+};
+
+// dW[e] tile (m0, n0) of 256 x 256 over one unit's K range, 128 per stage (four exponent rows
+// per operand).  8 waves of 128 x 64; the unit order and XCD bucketing follow the bf16
+// weight-gradient kernel.  WHICH only names the launch (0: dW2, 1: dW1) in kernel traces.
+template <int WHICH>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_mx_wg_kernel(const MxWgArgs g) {
+  constexpr int BM = 256, BN = 256, BK = 128, S = 2, WN = 4, NW = 8;
+  constexpr int TM = 128, TN = 64, FM = 4, FN = 2;
+  constexpr int A_BYTES = BK * BM, B_BYTES = BK * BN, E_BYTES = 4 * 256;
+  constexpr int STAGE = A_BYTES + B_BYTES + 2 * E_BYTES;
+  constexpr int QA = A_BYTES / (1024 * NW), QB = B_BYTES / (1024 * NW);
+  static_assert(QA == 4 && QB == 4, "DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
+
+  // ------------------------------------------------------------------ unit and tile
+  const int nN = g.N / BN, nM = g.Mo / BM, per_u = nM * nN;
+  const CONST_AS int32_t* meta = (const CONST_AS int32_t*)g.meta;
+  const int U = meta[0];
+  const int G_valid = U * per_u;
+  if ((int)blockIdx.x >= G_valid) return;
+  int pos = blockIdx.x, u;
+  if (meta[2]) {
+    // deal the units (largest first) to 8 buckets round-robin; XCD b takes bucket b's tiles
+    pos = xcd_remap(blockIdx.x, G_valid);
+    const int j = pos / per_u;
+    const int q = U / 8, r = U % 8;
+    int b, jb;
+    if (j < r * (q + 1)) {
+      b = j / (q + 1);
+      jb = j % (q + 1);
+    } else {
+      b = r + (j - r * (q + 1)) / q;
+      jb = (j - r * (q + 1)) % q;
+    }
+    u = b + 8 * jb;
+  } else {
+    u = pos / per_u;
+  }
+  const CONST_AS int32_t* up = (const CONST_AS int32_t*)g.units;
+  const int e = up[2 * u], kchunk = up[2 * u + 1];
+  const int t = pos % per_u;
+  int m0, nt;
+  if (nM % 8 == 0 || nN % 8 != 0) {
+    m0 = (t % nM) * BM;
+    nt = t / nM;
+  } else {
+    nt = t % nN;
+    m0 = (t / nN) * BM;
+  }
+  const int n0 = nt * BN;
+  const CONST_AS int32_t* pf = (const CONST_AS int32_t*)g.poff;
+  const int KC = meta[1];
+  const int kbeg = pf[e] + kchunk * KC;
+  const int kend = min(pf[e + 1], kbeg + KC);
+  const int pslot = ((const CONST_AS int32_t*)g.pslot)[e];
+  const int nk = (kend - kbeg) / BK;  // segments and chunks are multiples of 128 rows
+
+  // ------------------------------------------------------------------ DMA sources
+  // Operand instruction q of wave w: k rows 4*(4w+q) .. +3 of the stage, 16 lanes per row;
+  // lane l fills physical chunk l % 16 of its row from logical chunk (l % 16) ^ (2 * (row & 7)).
+  const uint8_t* a_src[QA];
+  const uint8_t* b_src[QB];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int kr = 4 * (wave * QA + q) + lane / 16;
+    const int c = (lane % 16) ^ (2 * (kr & 7));
+    a_src[q] = g.A + (int64_t)(kbeg + kr) * g.Mo + m0 + 16 * c;
+    b_src[q] = g.B + (int64_t)(kbeg + kr) * g.N + n0 + 16 * c;
+  }
+  // exponent row w % 4 of the stage: waves 0..3 for A, 4..7 for B; lane l brings 4 columns
+  const bool e_is_a = wave < 4;
+  const uint8_t* e_src = e_is_a ? g.Ae + (int64_t)(kbeg / 32 + wave) * g.Mo + m0 + 4 * lane
+                                : g.Be + (int64_t)(kbeg / 32 + wave - 4) * g.N + n0 + 4 * lane;
+  const int64_t e_ld = e_is_a ? g.Mo : g.N;
+  auto issue = [&](int it, int st) __attribute__((always_inline)) {
+    const int k0 = it * BK;
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, aebase = bbase + B_BYTES,
+                   bebase = aebase + E_BYTES;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) dma16(a_src[q] + (int64_t)k0 * g.Mo, abase + (wave * QA + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) dma16(b_src[q] + (int64_t)k0 * g.N, bbase + (wave * QB + q) * 1024);
+    dma4(e_src + (int64_t)(k0 / 32) * e_ld, (e_is_a ? aebase : bebase) + (wave & 3) * 256);
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Both operands are k-major: each fragment is a transpose read (read_kn8_mx), and lane l
+  // gives the exponent of its row (column) l % 32 for k block 2*kk + l/32 of the stage.  The
+  // B fragment is the MFMA's first operand, so the accumulators hold transposed blocks.
+  const int kbsel = lane >> 5;
+  auto compute = [&](int st) __attribute__((always_inline)) {
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, aebase = bbase + B_BYTES,
+                   bebase = aebase + E_BYTES;
+    i32x8 bv[2][FN];
+    int sb[2][FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int col = wn * TN + 32 * j;
+        bv[kk][j] = read_kn8_mx(bbase, col, kk, lane);
+        sb[kk][j] = *(const LDS_AS uint8_t*)(uintptr_t)(bebase + (2 * kk + kbsel) * 256 + col + (lane & 31));
+      }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * TM + 32 * i;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const i32x8 af = read_kn8_mx(abase, row, kk, lane);
+        const int sa = *(const LDS_AS uint8_t*)(uintptr_t)(aebase + (2 * kk + kbsel) * 256 + row + (lane & 31));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[kk][j], af, acc[i][j], 0, 0, 0, sb[kk][j], 0,
+                                                                      sa);
+      }
+    }
+  };
+
+  // ------------------------------------------------------------------ main loop (2 stages)
+  __syncthreads();
+  if (nk > 0) issue(0, 0);
+  for (int it = 0; it < nk; ++it) {
+    vm_lgkm_wait_barrier<0>();
+    if (it + 1 < nk) issue(it + 1, (it + 1) % S);
+    compute(it % S);
+  }
+
+  // ------------------------------------------------------------------ epilogue (registers)
+  // Lane l holds dW row m0 + wm*TM + 32*i + l%32 and, for r = 0..15, column
+  // n0 + wn*TN + 32*j + 8*(r/4) + 4*(l/32) + r%4.  An empty unit (no rows) stores zeros.
+  const int h = lane >> 5, lrow = lane & 31;
+  if (pslot >= 0) {
+    // one chunk of a split expert: fp32 partial, summed later in chunk order
+    float* out = g.partial + (int64_t)(pslot + kchunk) * g.Mo * g.N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float* orow = out + (int64_t)(m0 + wm * TM + 32 * i + lrow) * g.N + n0 + wn * TN;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(orow + 32 * j + 8 * q + 4 * h) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      uint16_t* orow = g.dW + ((int64_t)e * g.Mo + m0 + wm * TM + 32 * i + lrow) * g.N + n0 + wn * TN;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        // bf16 pairs, then lanes l and l+32 trade halves so each holds 8 consecutive columns
+        uint32_t p[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          p[q][0] = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          p[q][1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; a += 2)
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const auto r = __builtin_amdgcn_permlane32_swap(p[a][d], p[a + 1][d], false, false);
+            p[a][d] = r[0];
+            p[a + 1][d] = r[1];
+          }
+        *(uint4*)(orow + 32 * j + 8 * h) = make_uint4(p[0][0], p[0][1], p[1][0], p[1][1]);
+        *(uint4*)(orow + 32 * j + 16 + 8 * h) = make_uint4(p[2][0], p[2][1], p[3][0], p[3][1]);
+      }
+    }
+  }
+}
+
+hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st) {
+  mx_pad_offsets_kernel<<<1, 1024, 0, st>>>(offsets, E, poff);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_tokens(const uint16_t* src, int C, int gather, const MoeShape& s, const int32_t* offsets,
+                                  const int32_t* perm, const int32_t* poff, uint8_t* q, uint8_t* qe,
+                                  hipStream_t st) {
+  const int64_t blocks = mx_padded_rows((int64_t)s.T * s.k, s.E) / 32;
+  if (blocks == 0) return hipSuccess;
+  dim3 grid((unsigned)blocks, (unsigned)((C + 2047) / 2048));
+  mx_quant_tokens_kernel<<<grid, 256, 0, st>>>(src, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_wg(int which, const MoeShape& s, const uint8_t* Aq, const uint8_t* Ae, int Mo, const uint8_t* Bq,
+                        const uint8_t* Be, int N, const int32_t* poff, const WgSplit& sp, uint16_t* dW,
+                        hipStream_t st) {
+  MxWgArgs g{};
+  g.A = Aq;
+  g.Ae = Ae;
+  g.B = Bq;
+  g.Be = Be;
+  g.Mo = Mo;
+  g.N = N;
+  g.poff = poff;
+  g.units = sp.units;
+  g.meta = sp.meta;
+  g.pslot = sp.pslot;
+  g.partial = sp.partial;
+  g.dW = dW;
+  const int64_t blocks = (int64_t)(Mo / 256) * (N / 256) * (s.E + sp.max_partials);
+  if (blocks == 0) return hipSuccess;
+  if (which == 0) grouped_gemm_mx_wg_kernel<0><<<(unsigned)blocks, 512, 0, st>>>(g);
+  else grouped_gemm_mx_wg_kernel<1><<<(unsigned)blocks, 512, 0, st>>>(g);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -105,6 +105,14 @@ hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int col
                            uint8_t* qe, hipStream_t st);
 // Both orientations of [batch, rows, cols] in one pass (rows % 32 == 0, cols % 256 == 0):
 // column blocks into qc/qce, row blocks into qr/qre.
+// MXFP8 weight gradients: each expert's rows padded to a multiple of 128 (see gemm_mx.hip).
+inline int64_t mx_padded_rows(int64_t A, int E) { return (A + 127 * (int64_t)E + 127) / 128 * 128; }
+hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
+hipError_t launch_mx_quant_tokens(const uint16_t* src, int C, int gather, const MoeShape& s, const int32_t* offsets,
+                                  const int32_t* perm, const int32_t* poff, uint8_t* q, uint8_t* qe, hipStream_t st);
+hipError_t launch_mx_wg(int which, const MoeShape& s, const uint8_t* Aq, const uint8_t* Ae, int Mo, const uint8_t* Bq,
+                        const uint8_t* Be, int N, const int32_t* poff, const WgSplit& sp, uint16_t* dW,
+                        hipStream_t st);
 hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, int cols, uint8_t* qc, uint8_t* qce,
                                 uint8_t* qr, uint8_t* qre, hipStream_t st);
 hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe, const uint8_t* W1q,

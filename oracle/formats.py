@@ -123,3 +123,4 @@ def mx_roundtrip_rows(v: np.ndarray) -> np.ndarray:
     n = v.shape[0]
     vp = np.concatenate([v, np.zeros(((-n) % 32,) + v.shape[1:])], axis=0)
     return mx_dequantize(*mx_quantize(vp, 0), 0)[:n]
+

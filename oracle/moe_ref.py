@@ -148,10 +148,11 @@ def backward(x, W1, W2, ids, w, dy, logits_routed=True, W1_dx=None, W2_da=None, 
     da = (w dy) W2^T and the routing-weight gradient, W1_dx for dx = dH W1^T, x_dw for
     dW1 = x^T dH.  Left as None they are dy, W2, W1 and x.
 
-    q_dw, when given, is applied to each operand of the two weight-gradient products, one expert
-    at a time with its rows in the expert's sorted order: dW2[e] = q(As_e)^T q(dy_e) with
-    As_e = w * a (the routing-scaled activation the down projection consumes) and dW1[e] =
-    q(x_e)^T q(dH_e).  A layer that quantises those operands along the token axis, in blocks
+    q_dw, when given, is applied to the layer inputs that enter the two weight-gradient
+    products, one expert at a time with its rows in the expert's sorted order: dW2[e] =
+    As_e^T q(dy_e) with As_e = w * a (the routing-scaled activation the down projection
+    consumes) and dW1[e] = q(x_e)^T dH_e.  The intermediates As and dH stay exact, as they do
+    everywhere in this oracle.  A layer that quantises the inputs along the token axis, in blocks
     that stay inside one expert, is modelled by q_dw = mx_roundtrip_rows."""
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
@@ -184,12 +185,12 @@ def backward(x, W1, W2, ids, w, dy, logits_routed=True, W1_dx=None, W2_da=None, 
         if q_dw is None:
             dW2[e] = a.T @ (wf[P][:, None] * dy[R])
         else:
-            dW2[e] = q_dw(wf[P][:, None] * a).T @ q_dw(dy[R])
+            dW2[e] = (wf[P][:, None] * a).T @ q_dw(dy[R])
         da = (wf[P][:, None] * dYa) @ W2_da[e].T
         dG = da * U * sg * (1.0 + G * (1.0 - sg))      # d silu / dg = sig * (1 + g (1 - sig))
         dU = da * S
         dH = np.concatenate([dG, dU], axis=1)
-        dW1[e] = x_dw[R].T @ dH if q_dw is None else q_dw(x_dw[R]).T @ q_dw(dH)
+        dW1[e] = (x_dw[R] if q_dw is None else q_dw(x_dw[R])).T @ dH
         np.add.at(dx, R, dH @ W1_dx[e].T)
     out = dict(dx=dx, dW1=dW1, dW2=dW2, d_topk_w=dw.reshape(T, k), plan=pl)
     if logits_routed:

@@ -49,8 +49,10 @@ def _mx_oracle(inp):
     ids, w = oracle.route(inp.logits, inp.k)
     y = oracle.forward(xq, W1f, W2f, ids, w)
     # H from the forward's operands; dA from dy and W2 in blocks along d; dX with W1 in blocks
-    # along 2f; the weight gradients multiply the bf16 x and dy
-    bw = oracle.backward(xq, W1f, W2f, ids, w, dy, W1_dx=W1b, W2_da=W2b, dy_da=dyq, x_dw=x)
+    # along 2f; the weight gradients take x and dy in blocks along the token axis, inside each
+    # expert (the layer also quantises As and dH there; the oracle keeps them exact)
+    bw = oracle.backward(xq, W1f, W2f, ids, w, dy, W1_dx=W1b, W2_da=W2b, dy_da=dyq, x_dw=x,
+                         q_dw=oracle.mx_roundtrip_rows)
     return dict(ids=ids, w=w, plan=bw["plan"], y=y, dx=bw["dx"], d_topk_w=bw["d_topk_w"], d_logits=bw["d_logits"],
                 dW1=bw["dW1"], dW2=bw["dW2"])
 
@@ -130,6 +132,17 @@ def test_mx_fullsize_qwen3():
     lhs = float((gl.dy.double() * b["y"].double()).sum())
     mid = float((b["topk_w"].double() * b["d_topk_w"].double()).sum())
     errs["sum(w*dw)"] = abs(mid - lhs) / float(gl.dy.double().abs().mul(b["y"].double().abs()).sum())
+    # two experts' weight gradients in full, with token-axis operand blocks
+    x = oracle.bf16_to_f64(inp.x)
+    xq_all = oracle.mx_dequantize(*oracle.mx_quantize(x, 1), 1)
+    dy = oracle.bf16_to_f64(inp.dy)
+    dyq_all = oracle.mx_dequantize(*oracle.mx_quantize(dy, 1), 1)
+    dW1, dW2 = b["dW1"], b["dW2"]
+    for e in (0, inp.E - 1):
+        r1, r2 = oracle.expert_weight_grads(xq_all, W1f, W2f, ids, w, dy, e, W2_da=W2b, dy_da=dyq_all, x_dw=x,
+                                            q_dw=oracle.mx_roundtrip_rows)
+        errs[f"dW1[{e}]"] = rel_err(to_np(dW1[e]), r1)
+        errs[f"dW2[{e}]"] = rel_err(to_np(dW2[e]), r2)
     print("[case] qwen3 MXFP8: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL_FP8}
     assert not bad, bad

@@ -198,15 +198,15 @@ def test_backward_q_dw_identity_and_scaling():
     for key in ("dW1", "dW2"):                       # As^T dy = a^T (w dy): only the grouping moves
         np.testing.assert_allclose(same[key], base[key], rtol=1e-12, atol=1e-12)
     dbl = oracle.backward(x, W1, W2, ids, w, dy, q_dw=lambda v: 2.0 * v)
-    for key in ("dW1", "dW2"):                       # both operands of each product pass through q
-        np.testing.assert_allclose(dbl[key], 4.0 * base[key], rtol=1e-12, atol=1e-12)
+    for key in ("dW1", "dW2"):                       # one operand of each product (x, dy) passes through q
+        np.testing.assert_allclose(dbl[key], 2.0 * base[key], rtol=1e-12, atol=1e-12)
     for key in ("dx", "d_topk_w", "d_logits"):
         np.testing.assert_array_equal(dbl[key], base[key])
 
 
 def test_backward_q_dw_one_expert_by_hand():
-    """dW2[e] and dW1[e] with row-block MX operands, rebuilt from per-row loops and the brute-force
-    quantiser, in the expert's token order."""
+    """dW2[e] = As^T q(dy) and dW1[e] = q(x)^T dH with row-block MX inputs, rebuilt from per-row
+    loops and the brute-force quantiser, in the expert's token order."""
     x, dy, W1, W2, ids, w = _tiny_layer(9)
     f = W2.shape[1]
     out = oracle.backward(x, W1, W2, ids, w, dy, q_dw=oracle.mx_roundtrip_rows)
@@ -223,8 +223,8 @@ def test_backward_q_dw_one_expert_by_hand():
             dH.append(np.concatenate([da * ut * sg * (1.0 + gt * (1.0 - sg)), da * gt * sg]))
         As, dH = np.array(As), np.array(dH)
         q = _brute_roundtrip_rows
-        np.testing.assert_allclose(out["dW2"][e], q(As).T @ q(dy[rows]), rtol=1e-12, atol=1e-12)
-        np.testing.assert_allclose(out["dW1"][e], q(x[rows]).T @ q(dH), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out["dW2"][e], As.T @ q(dy[rows]), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out["dW1"][e], q(x[rows]).T @ dH, rtol=1e-12, atol=1e-12)
     assert max(sum(ids[:, 0] == e) for e in range(3)) > 32          # a block boundary was crossed
 
 
@@ -236,3 +236,4 @@ def test_expert_weight_grads_matches_backward():
             dW1, dW2 = oracle.expert_weight_grads(x, W1, W2, ids, w, dy, e, q_dw=q)
             np.testing.assert_allclose(dW1, full["dW1"][e], rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(dW2, full["dW2"][e], rtol=1e-12, atol=1e-12)
+
