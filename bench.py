@@ -56,8 +56,9 @@ STAGE_KERNEL_BF16 = {"gemm_up": "moe::grouped_gemm_kernel<0,", "gemm_down": "moe
                      "tokrow": "moe::tokrow_kernel", "permute": "moe::permute_kernel"}
 STAGE_KERNEL_FP8 = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_fp8_kernel<0>",
                         gemm_down="moe::grouped_gemm_fp8_kernel<1>", gemm_dact="moe::grouped_gemm_fp8_kernel<2>",
-                        gemm_dx="moe::grouped_gemm_fp8_kernel<3>", quant_dy="moe::quant_rows_kernel",
-                        dequant_x="moe::dequant_rows_kernel")
+                        gemm_dx="moe::grouped_gemm_fp8_kernel<3>", gemm_dw2="moe::grouped_gemm_mx_wg_kernel<0>",
+                        gemm_dw1="moe::grouped_gemm_mx_wg_kernel<1>", quant_dy="moe::quant_rows_kernel",
+                        mx_quant_t="moe::mx_quant_tokens", mx_pad="moe::mx_pad_offsets")
 FP8_STAGES = ("gemm_up", "gemm_down", "gemm_dact", "gemm_dx")
 
 
@@ -84,9 +85,8 @@ def is_fp8(config):
 
 
 def stage_dtype(config, stage):
-    if config.endswith(":mxfp8"):      # every GEMM, weight gradients included, runs MXFP8
-        return "fp8" if stage in MX_FP8_STAGES else "bf16"
-    return "fp8" if (is_fp8(config) and stage in FP8_STAGES) else "bf16"
+    # both fp8 formats run every GEMM in fp8, the weight gradients as MXFP8
+    return "fp8" if (is_fp8(config) and stage in MX_FP8_STAGES) else "bf16"
 
 
 def stage_kernels(config):
@@ -95,7 +95,7 @@ def stage_kernels(config):
     return STAGE_KERNEL_FP8 if is_fp8(config) else STAGE_KERNEL_BF16
 
 
-def stage_bytes(stage, T, d, f, E, k, A):
+def stage_bytes(stage, T, d, f, E, k, A, fp8_in=False):
     """Algorithmic HBM bytes of one launch of a bandwidth-bound stage (each byte the stage
     must read or write once; A = routed pairs)."""
     if stage in ("combine", "combine_dx"):
@@ -108,8 +108,6 @@ def stage_bytes(stage, T, d, f, E, k, A):
         return T * k * 4 * 3 + T * E * 4
     if stage == "quant_dy":
         return T * d * 2 + T * d + T * (d // 128) * 4
-    if stage == "dequant_x":
-        return T * d + T * (d // 128) * 4 + T * d * 2
     if stage in ("mx_quant_x", "mx_quant_dy"):
         return T * d * 2 + T * d + T * d // 32
     if stage == "mx_quant_as_t":                            # sorted rows in, token-axis blocks out
@@ -117,7 +115,7 @@ def stage_bytes(stage, T, d, f, E, k, A):
     if stage == "mx_quant_dh_t":
         return A * 2 * f * 2 + A * 2 * f + A * 2 * f // 32
     if stage in ("mx_quant_x_t", "mx_quant_dy_t"):           # each token row read once, A rows out
-        return T * d * 2 + A * d + A * d // 32
+        return T * d * (1 if (stage == "mx_quant_x_t" and fp8_in) else 2) + A * d + A * d // 32
     if stage in ("mx_quant_w1", "mx_quant_w2"):
         return E * d * f * (2 + 1) + E * d * f // 32     # one of W1 (2df) / W2 (df): bytes of W1 halved
     return None
@@ -457,7 +455,7 @@ def main():
             ent["frac_mfma_peak"] = ent["tflops"] / pk
             ideal_ms += fl / (pk * 1e12) * 1e3
         else:
-            by = stage_bytes(stage, T, d, f, E, k, A)
+            by = stage_bytes(stage, T, d, f, E, k, A, fp8_in=fp8)
             if by:
                 ent["gbs"] = by / (avg * 1e-3) / 1e9
         stages[stage] = ent
@@ -474,7 +472,7 @@ def main():
                 "frac": achieved / pk, "traffic": traffic, "dtype": stage_dtype(run_name, dom),
                 "algorithmic_flop_per_launch": fl, "avg_launch_ms": dom_e["avg_ms"]}
     else:
-        by = stage_bytes(dom, T, d, f, E, k, A)
+        by = stage_bytes(dom, T, d, f, E, k, A, fp8_in=fp8)
         achieved = by / (dom_e["avg_ms"] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": by,

@@ -521,41 +521,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   }
 }
 
-// x (e4m3 with 1x128 scales) -> bf16, for the weight gradient.
-__global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__ qs,
-                                                           int64_t n8, int cols, uint16_t* __restrict__ dst) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const u32x2 w = *(const u32x2*)(q + i * 8);
-  const int64_t row = (i * 8) / cols, blk = ((i * 8) % cols) / 128;
-  const float s = qs[row * (cols / 128) + blk];
-  float f[8];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t word = h ? w.y : w.x;
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-    f[4 * h] = a[0] * s;
-    f[4 * h + 1] = a[1] * s;
-    f[4 * h + 2] = b[0] * s;
-    f[4 * h + 3] = b[1] * s;
-  }
-  *(uint4*)(dst + i * 8) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                                      pack_bf16x2(f[6], f[7]));
-}
-
 hipError_t launch_quant_rows(const uint16_t* src, int64_t rows, int cols, uint8_t* q, float* qs, hipStream_t st) {
   const int64_t n8 = rows * cols / 8;
   if (n8 == 0) return hipSuccess;
   quant_rows_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(src, n8, cols, q, qs);
-  return hipGetLastError();
-}
-
-hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, int cols, uint16_t* dst,
-                               hipStream_t st) {
-  const int64_t n8 = rows * cols / 8;
-  if (n8 == 0) return hipSuccess;
-  dequant_rows_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(q, qs, n8, cols, dst);
   return hipGetLastError();
 }
 

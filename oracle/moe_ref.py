@@ -245,9 +245,11 @@ def token_backward(x_row, W1, W2, ids_row, w_row, dy_row, W1_dx=None, W2_da=None
     return dx, dw
 
 
-def weight_grad_entries(x, W1, W2, ids, w, dy, e, rows_i, cols_j, which):
+def weight_grad_entries(x, W1, W2, ids, w, dy, e, rows_i, cols_j, which, q_dw=None):
     """Selected entries of dW1[e] (which='dW1', i over d, j over 2f) or dW2[e] (which='dW2',
-    i over f, j over d), computed from the expert's token rows only."""
+    i over f, j over d), computed from the expert's token rows only.  q_dw as in backward(): it
+    acts on the expert's rows of one input column at a time (x column i for dW1, dy column j
+    for dW2), which is all an entry needs because its blocks run down that column."""
     k = ids.shape[1]
     f = W2.shape[1]
     flat = np.asarray(ids).ravel()
@@ -264,7 +266,8 @@ def weight_grad_entries(x, W1, W2, ids, w, dy, e, rows_i, cols_j, which):
             g = Xe @ W1[e][:, i]
             u = Xe @ W1[e][:, f + i]
             a_i = g * _sigmoid(g) * u
-            out[n] = np.sum(a_i * wv * dYe[:, j])
+            dcol = dYe[:, j] if q_dw is None else q_dw(dYe[:, [j]])[:, 0]
+            out[n] = np.sum(wv * a_i * dcol)
         else:
             c = j % f                                   # column pair (gate c, up f + c)
             g = Xe @ W1[e][:, c]
@@ -272,7 +275,8 @@ def weight_grad_entries(x, W1, W2, ids, w, dy, e, rows_i, cols_j, which):
             sg = _sigmoid(g)
             da = wv * (dYe @ W2[e][c, :])
             dh = da * u * sg * (1.0 + g * (1.0 - sg)) if j < f else da * g * sg
-            out[n] = np.sum(Xe[:, i] * dh)
+            xcol = Xe[:, i] if q_dw is None else q_dw(Xe[:, [i]])[:, 0]
+            out[n] = np.sum(xcol * dh)
     return out
 
 

@@ -237,3 +237,16 @@ def test_expert_weight_grads_matches_backward():
             np.testing.assert_allclose(dW1, full["dW1"][e], rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(dW2, full["dW2"][e], rtol=1e-12, atol=1e-12)
 
+
+
+def test_weight_grad_entries_with_q_dw_match_backward():
+    x, dy, W1, W2, ids, w = _tiny_layer(12, k=2)
+    full = oracle.backward(x, W1, W2, ids, w, dy, q_dw=oracle.mx_roundtrip_rows)
+    g = np.random.default_rng(13)
+    for e in range(W1.shape[0]):
+        ri, cj = g.integers(0, x.shape[1], 12), g.integers(0, 2 * W2.shape[1], 12)
+        got = oracle.weight_grad_entries(x, W1, W2, ids, w, dy, e, ri, cj, "dW1", q_dw=oracle.mx_roundtrip_rows)
+        np.testing.assert_allclose(got, full["dW1"][e][ri, cj], rtol=1e-12, atol=1e-12)
+        ri, cj = g.integers(0, W2.shape[1], 12), g.integers(0, x.shape[1], 12)
+        got = oracle.weight_grad_entries(x, W1, W2, ids, w, dy, e, ri, cj, "dW2", q_dw=oracle.mx_roundtrip_rows)
+        np.testing.assert_allclose(got, full["dW2"][e][ri, cj], rtol=1e-12, atol=1e-12)
