@@ -65,6 +65,27 @@ def test_mx_layer_parity(name):
     T, d, f, E, k, seed = CASES[name]
     inp = make_inputs(T, d, f, E, k, seed=seed)
     print(f"[case] {name} T={T} d={d} f={f} E={E} k={k}", flush=True)
+    _check_mx_layer(name, inp)
+
+
+@pytest.mark.parametrize("T,k", [(2600, 2), (5000, 1)])
+def test_mx_heavy_and_empty_experts(T, k):
+    """One expert over the 2048-row weight-gradient chunk (its padded segment split in two or
+    three fp32 partials summed in chunk order) and two experts with no rows (zero gradients)."""
+    E = 8
+    bias = np.zeros(E, np.float32)
+    bias[1], bias[5], bias[6] = 10.0, -30.0, -30.0
+    inp = make_inputs(T, 256, 256, E, k, seed=44, logits_bias=bias)
+    print(f"[case] mx heavy/empty experts T={T} k={k}", flush=True)
+    gl = _check_mx_layer(f"heavy{T}", inp)
+    counts = gl.routing_np()["counts"]
+    assert counts[1] > 2048 and counts[5] == 0 and counts[6] == 0
+    for e in (5, 6):
+        assert torch.all(gl.b["dW1"][e] == 0) and torch.all(gl.b["dW2"][e] == 0)
+
+
+def _check_mx_layer(name, inp):
+    E = inp.E
     gl = GpuLayer(inp, dtype=moe.MOE_MXFP8).run()
     ref = _mx_oracle(inp)
     check_routing_bitexact(gl, ref["ids"], ref["plan"])
@@ -81,6 +102,7 @@ def test_mx_layer_parity(name):
           f", max dW {max(v for k, v in errs.items() if k.startswith('dW')):.2e}", flush=True)
     bad = {k: v for k, v in errs.items() if not v <= TOL_FP8}
     assert not bad, bad
+    return gl
 
 
 class _MxExperts:
