@@ -54,8 +54,8 @@
  *     smallest power of two that brings its maximum magnitude within 448 (no clipping); elements
  *     round to nearest even.  The data-gradient GEMMs use weights quantised along their own K;
  *     moe_forward produces both quantisations in one pass over each weight matrix and keeps
- *     the backward's in `saved`.  Weight gradients are computed from bf16 operands.  d and f
- *     must be multiples of 256.
+ *     the backward's in `saved`.  Weight gradients run in MXFP8 too, quantised along their K,
+ *     the token axis (see moe_backward).  d and f must be multiples of 256.
  *   - Alignment (MOE_ERR_ALIGN otherwise): tensors 16-byte aligned, ws and saved 256-byte
  *     aligned (every torch/hipMalloc allocation is).
  */
@@ -140,8 +140,11 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale,
  * kept logits; topk_ids is then required).  `saved` must come from moe_forward on the same
  * inputs.  Every reduction has a fixed order, so results are bitwise reproducible.
  * fp8: dy is quantised like the forward activations (1x128 blocks) for the two data-gradient
- * GEMMs and dH is requantised the same way between them; the weight gradients use bf16
- * operands (the saved bf16 activations, dy, dH and x dequantised). */
+ * GEMMs and dH is requantised the same way between them.
+ * Weight gradients, fp8 and MXFP8: dW2 = As^T dy and dW1 = x^T dH run as MXFP8 GEMMs whose K is
+ * the expert's rows; both operands are quantised in blocks of 32 consecutive sorted rows that
+ * never straddle two experts ([JAX] "Csoportosított mátrixszorzás és összevont adatmozgatás":
+ * group-aware quantisation).  For MOE_FP8_E4M3, x enters as code * scale in fp32. */
 int moe_backward(const moe_dims* dims, const void* dy, const void* x, const float* x_scale,
                  const void* W1, const float* W1_scale, const void* W2, const float* W2_scale,
                  const int32_t* topk_ids, const float* topk_w, const int32_t* offsets,
