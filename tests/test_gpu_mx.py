@@ -180,3 +180,15 @@ def test_mx_bitwise_determinism():
         a = v.view(torch.uint8) if v.dtype != torch.uint8 else v
         b = gl.b[k].view(torch.uint8) if gl.b[k].dtype != torch.uint8 else gl.b[k]
         assert torch.equal(a, b), k
+
+
+def test_mx_zero_tokens():
+    # no token: every expert's weight gradient is exactly zero and nothing else is touched
+    inp = make_inputs(0, 256, 256, 4, 2, seed=45)
+    print("[case] mx T=0", flush=True)
+    gl = GpuLayer(inp, dtype=moe.MOE_MXFP8)
+    gl.b["dW1"].fill_(3.0)
+    gl.b["dW2"].fill_(3.0)
+    gl.run()
+    assert torch.all(gl.b["offsets"] == 0)
+    assert torch.all(gl.b["dW1"] == 0) and torch.all(gl.b["dW2"] == 0)
