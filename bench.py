@@ -317,6 +317,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="steps timed one by one after a 512 MiB cache-flushing write (0: skip)")
     ap.add_argument("--config", default="qwen3", choices=sorted(WORKLOADS))
     ap.add_argument("--dtype", default="auto", choices=["auto", "mxfp8"],
                     help="auto: the workload's own format; mxfp8: run a bf16 workload as MXFP8 (quantised inside)")
@@ -497,6 +499,26 @@ def main():
                    "frac_hbm_peak": pby / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del xp
 
+    # LLC-cold steps: a 512 MiB scratch write before each one (outside its timing) evicts the
+    # step's operands from the 256 MB last-level cache and the L2s; the median step is reported
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cts = []
+        for i in range(args.cold_steps):
+            scratch.fill_(i & 0xFF)
+            c0.record(cur)
+            step()
+            c1.record(cur)
+            torch.cuda.synchronize()
+            cts.append(c0.elapsed_time(c1))
+        cms = sorted(cts)[len(cts) // 2]
+        cold = {"ms_per_step": cms, "value": useful / (cms * 1e-3) / 1e12, "unit": "TFLOPS",
+                "steps": args.cold_steps, "statistic": "median", "flush_bytes_between_steps": 512 << 20}
+        log(f"[bench] LLC-cold: {cms:.3f} ms/step (median of {args.cold_steps})")
+        del scratch
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f}s sample) ...")
@@ -514,7 +536,7 @@ def main():
         "frac_of_bf16_peak": tflops / PEAK_TFLOPS["bf16"],
         "frac_of_mfma_peak": ideal_ms / ms,
         "useful_flop_per_step": useful, "stages": stages, "permute_standalone": permute, "roofline": roof,
-        "cpu_baseline": cpu,
+        "llc_cold": cold, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
