@@ -167,6 +167,17 @@ def _host_cores():
     return max(1, min(16, n))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, target_s: float):
     """The fp64 oracle (route or plan, forward, backward) on the first n tokens, with n grown
     from 256 until one timed run takes at least half of target_s (the last run is reported)."""
@@ -213,7 +224,7 @@ def cpu_baseline(inp, target_s: float):
                 break
             n = int(min(inp.T, max(2 * n, n * target_s / max(dt, 1e-3))))
     return {"value": 18.0 * pairs * inp.d * inp.f / dt / 1e12, "unit": "TFLOPS", "cores": int(threads),
-            "kind": "oracle", "tokens_per_s": n / dt, "seconds": dt,
+            "kind": "oracle", "tokens_per_s": n / dt, "seconds": dt, "cpu_model": _cpu_model(),
             "sample": f"first {n} of {inp.T} tokens of the same workload ({pairs} routed pairs, all {inp.E} "
                       f"experts), {'plan' if fp8 else 'route+plan'}+forward+backward in fp64 numpy on "
                       f"{'exactly dequantised fp8 inputs' if fp8 else 'bf16 inputs'}, {threads} BLAS threads"}
