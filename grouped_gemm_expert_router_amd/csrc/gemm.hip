@@ -15,11 +15,12 @@
 //   DACT  G  = dy[tok] W2[e]^T     ragged M, A gathered, B = W2 rows (K contiguous); dSwiGLU epilogue
 //   DX    dXp = dH W1[e]^T         ragged M, B = W1 rows (K contiguous); rows stored in slot order
 //   WG    dW = P_e^T Q_e           ragged K = the expert's rows; both operands row-major over K
-// Tiles are BM x BN x BK; 4 waves in a WM x WN grid each own (BM/WM) x (BN/WN) of the tile as
-// 32x32 MFMA blocks.  Both operand tiles live in LDS K-contiguous per row with a 16-byte-chunk
-// XOR swizzle (chunk ^ row%8), so every MFMA operand is one ds_read_b128.  Operands whose
-// global layout is not K-contiguous are transposed in registers (4x8 blocks of bf16) on their
-// way into LDS.  Two LDS stages: global loads for tile k+1 are in flight during tile k's MFMAs.
+// Tiles are BM x BN x BK (256 x 256 x 64 where the shape allows); the waves of a WM x WN grid
+// each own (BM/WM) x (BN/WN) of the tile as 32x32 MFMA blocks.  Operand tiles go from global
+// memory straight into LDS (global_load_lds_dwordx4), in their global orientation, with a
+// 16-byte-chunk XOR swizzle: a K-contiguous tile is read as one ds_read_b128 per MFMA operand,
+// an M- or N-contiguous one with the gfx950 transpose read ds_read_b64_tr_b16.  Two LDS stages:
+// the DMA of k step t+1 is in flight during step t's MFMAs.  Epilogues store from registers.
 #include "common.hpp"
 #include "gemm_common.hpp"
 #include "kernels.hpp"
