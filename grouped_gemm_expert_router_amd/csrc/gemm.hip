@@ -329,6 +329,9 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     constexpr int KS = BK / 16;
     bf16x8_t af[2][FM], bv[2][FN];
     load_frags(abase, bbase, 0, af[0], bv[0]);
+    // Raised wave priority while the MFMAs issue: with two waves per SIMD, the arbiter then
+    // favours the wave that feeds the matrix pipe over one issuing its DMA.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int cur = kk & 1;
@@ -343,6 +346,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
       if (kk + 1 < KS) sched_interleave<FM * FN, FM * (A_KN ? 2 : 1) + FN * (B_KN ? 2 : 1)>();
 #endif
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ------------------------------------------------------------------ main loop
