@@ -32,6 +32,8 @@ int check_dims(const moe_dims* d) {
   const int bm = d->dtype != MOE_BF16 ? kFp8BM : kGemmBM;
   const int64_t rows = (A + bm - 1) / bm + (A < d->E ? A : d->E);
   if (rows * (d->f / 64 > d->d / 128 ? d->f / 64 : d->d / 128) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  // the fp8 weight gradients index the 128-padded expert segments with 32-bit rows
+  if (d->dtype != MOE_BF16 && mx_padded_rows(A, (int)d->E) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 

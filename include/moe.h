@@ -42,7 +42,7 @@
  *     a launch failed (moe_status_string() then names the HIP error).
  *   - Shapes (MOE_ERR_SHAPE otherwise): T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64),
  *     d and f positive multiples of 128 (MOE_FP8_E4M3, MOE_MXFP8: of 256) and at most 65536,
- *     T*k < 2^31.
+ *     T*k < 2^31 (MOE_FP8_E4M3, MOE_MXFP8: T*k + 127*E rounded up to 128 < 2^31).
  *   - fp8 (MOE_FP8_E4M3): codes are OCP e4m3 (bias 7, max 448, no infinities); a block's value
  *     is code * scale with its fp32 scale ([Prime] "Mit csinált a Prime Intellect?": blockwise
  *     FP8 is one of the kernel's data types).  Outputs and gradients stay bf16/fp32.

@@ -74,7 +74,8 @@ def test_fp8_shape_rules(lib):
     assert sz(lib, moe.dims(64, 256, 384, 8, 2, dtype=moe.MOE_FP8_E4M3), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
     bf = moe.dims(64, 256, 256, 8, 2)
     f8 = moe.dims(64, 256, 256, 8, 2, dtype=moe.MOE_FP8_E4M3)
-    # fp8 adds the e4m3 copies of As (forward) and of dy, dH plus bf16 x (backward)
+    # fp8 adds the e4m3 copies of As (forward) and of dy, dH plus the token-axis operand buffers
+    # of the weight gradients (backward)
     A, d, f = 128, 256, 256
     assert sz(lib, f8, moe.MOE_WS_FORWARD)[1] >= sz(lib, bf, moe.MOE_WS_FORWARD)[1] + A * f + A * (f // 128) * 4
     assert sz(lib, f8, moe.MOE_WS_BACKWARD)[1] >= sz(lib, bf, moe.MOE_WS_BACKWARD)[1] + 64 * d * 3 + A * 2 * f
@@ -164,3 +165,13 @@ def test_mxfp8_argument_rules(lib):
     assert q(None, 1, 64, 64, 1, F, F) == moe.MOE_ERR_NULL
     assert q(F, 1, 64, 64, 1, F + 8, F) == moe.MOE_ERR_ALIGN
     assert q(F, 0, 64, 64, 1, None, None) == moe.MOE_OK         # empty input: nothing to do
+
+
+def test_fp8_padded_rows_rule(lib):
+    # T*k = 2^31 - 1000 pairs is a legal bf16 layer; the fp8 formats pad each expert's rows to a
+    # multiple of 128 for the weight gradients, which would pass 2^31 with 1024 experts
+    T, k, E = 268435331, 8, 1024
+    assert sz(lib, moe.dims(T, 256, 256, E, k), moe.MOE_WS_FORWARD)[0] == moe.MOE_OK
+    for dt in (moe.MOE_FP8_E4M3, moe.MOE_MXFP8):
+        assert sz(lib, moe.dims(T, 256, 256, E, k, dtype=dt), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
+        assert sz(lib, moe.dims(T // 2, 256, 256, E, k, dtype=dt), moe.MOE_WS_FORWARD)[0] == moe.MOE_OK
