@@ -105,17 +105,12 @@ def test_fp8_fullsize_dsv3_share():
     errs = {"y": rel_err(to_np(b["y"])[toks], y_o),
             "dx": rel_err(to_np(b["dx"])[toks], np.stack([a for a, _ in bw])),
             "d_topk_w": rel_err(to_np(b["d_topk_w"])[toks], np.stack([c for _, c in bw]))}
-    experts = np.unique(np.concatenate([[int(np.argmax(pl.counts)), int(np.argmin(pl.counts))],
-                                        g.choice(inp.E, 3, replace=False)]))
-    for e in experts:
-        ri, cj = g.integers(0, inp.d, 10), g.integers(0, 2 * inp.f, 10)
-        ref = oracle.weight_grad_entries(x, W1, W2, ids, w, dy, e, ri, cj, "dW1", q_dw=oracle.mx_roundtrip_rows)
-        got = b["dW1"][e][torch.from_numpy(ri).cuda(), torch.from_numpy(cj).cuda()].float().cpu().numpy()
-        errs[f"dW1[{e}]"] = rel_err(got, ref)
-        ri, cj = g.integers(0, inp.f, 10), g.integers(0, inp.d, 10)
-        ref = oracle.weight_grad_entries(x, W1, W2, ids, w, dy, e, ri, cj, "dW2", q_dw=oracle.mx_roundtrip_rows)
-        got = b["dW2"][e][torch.from_numpy(ri).cuda(), torch.from_numpy(cj).cuda()].float().cpu().numpy()
-        errs[f"dW2[{e}]"] = rel_err(got, ref)
+    # the largest and the smallest expert's weight gradients in full (their whole slices set the
+    # error scale), with the token-axis MX blocks of x and dy the layer uses
+    for e in (int(np.argmax(pl.counts)), int(np.argmin(pl.counts))):
+        r1, r2 = oracle.expert_weight_grads(x, W1, W2, ids, w, dy, e, q_dw=oracle.mx_roundtrip_rows)
+        errs[f"dW1[{e}]"] = rel_err(to_np(b["dW1"][e]), r1)
+        errs[f"dW2[{e}]"] = rel_err(to_np(b["dW2"][e]), r2)
     # y is linear in the routing weights: sum(dy * y) = sum(w * d_topk_w)
     lhs = float((gl.dy.double() * b["y"].double()).sum())
     mid = float((b["topk_w"].double() * b["d_topk_w"].double()).sum())
