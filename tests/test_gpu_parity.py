@@ -37,6 +37,9 @@ CASES = {
     # limits of the ABI: the most experts (most of them empty) and the largest k (= E)
     "max_experts": (96, 128, 128, 1024, 4, 14),
     "max_k": (24, 128, 128, 64, 64, 15),
+    # more 256x256 output tiles than compute units in each ragged-M product (288 each), with
+    # ragged row tails in every expert
+    "tiles_beyond_one_per_cu": (4000, 768, 384, 8, 6, 16),
 }
 
 
