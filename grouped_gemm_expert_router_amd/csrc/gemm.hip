@@ -263,33 +263,42 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
         dma16(src, bbase + (wave * QB + q) * 1024);
       }
     } else {
-      int tk[KRW];
+      // token rows of the wave's KRW k rows, one scalar load
+      i32x8 tk = {0, 0, 0, 0, 0, 0, 0, 0};
       if (g.gatherA || g.gatherB) {
         if constexpr (KRW == 8) {
-          const i32x8 v = *(const CONST_AS i32x8*)(g.tokrow + kbeg + k0 + KRW * wave);
-#pragma unroll
-          for (int z = 0; z < 8; ++z) tk[z] = v[z];
+          tk = *(const CONST_AS i32x8*)(g.tokrow + kbeg + k0 + KRW * wave);
         } else {
           const i32x4 v = *(const CONST_AS i32x4*)(g.tokrow + kbeg + k0 + KRW * wave);
-#pragma unroll
-          for (int z = 0; z < 4; ++z) tk[z] = v[z];
+          tk = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
         }
       }
-      auto row_of = [&](int kr, bool gather) __attribute__((always_inline)) -> int64_t {
-        const int lk = kr - KRW * wave;  // 0..KRW-1
+      // Instruction q of an operand with C columns covers k rows KRW*wave + R*q + r, where
+      // R = 512/C rows per instruction and r = lane / (C/8): the lane's token is one of R
+      // elements at fixed positions (a two-way select for C = 256).  Selecting with fixed
+      // indices keeps the values in registers; a select on a computed index (k row - KRW*wave)
+      // is turned by the compiler into an indexed array in LDS, one LDS round trip per DMA.
+      auto tok_sel = [&](int q, int R, int CHL) __attribute__((always_inline)) -> int {
+        int t = tk[R * q];
+        const int r = lane / CHL;
+#pragma unroll
+        for (int z = 1; z < 4; ++z)
+          if (z < R) t = (r == z) ? tk[R * q + z] : t;
+        return t;
+      };
+      auto row_of = [&](int kr, int t, bool gather) __attribute__((always_inline)) -> int64_t {
         const bool ok = k0 + kr < klen;
         if (!gather) return ok ? (int64_t)(kbeg + k0 + kr) : (int64_t)kbeg;
-        int t8 = tk[0];
-#pragma unroll
-        for (int z = 1; z < KRW; ++z) t8 = (lk == z) ? tk[z] : t8;
-        return ok ? (int64_t)t8 : (int64_t)tok_first;
+        return ok ? (int64_t)t : (int64_t)tok_first;
       };
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        dma16(g.A + row_of(a_kr[q], g.gatherA) * g.lda + a_col[q], abase + (wave * QA + q) * 1024);
+        dma16(g.A + row_of(a_kr[q], tok_sel(q, 512 / BM, BM / 8), g.gatherA) * g.lda + a_col[q],
+              abase + (wave * QA + q) * 1024);
 #pragma unroll
       for (int q = 0; q < QB; ++q)
-        dma16(g.B + row_of(b_kr[q], g.gatherB) * g.ldb + b_col[q], bbase + (wave * QB + q) * 1024);
+        dma16(g.B + row_of(b_kr[q], tok_sel(q, 512 / BN, BN / 8), g.gatherB) * g.ldb + b_col[q],
+              bbase + (wave * QB + q) * 1024);
     }
   };
 
