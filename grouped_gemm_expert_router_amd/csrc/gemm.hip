@@ -251,7 +251,20 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   int tok_first = 0;
   if constexpr (RAGGED_K)
     if (klen > 0 && (g.gatherA || g.gatherB)) tok_first = ((const CONST_AS int32_t*)g.tokrow)[kbeg];
-  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+  // Ragged K: the tokens of the wave's KRW k rows of step t, one scalar load.
+  auto load_tk = [&](int t) __attribute__((always_inline)) -> i32x8 {
+    i32x8 tk = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (RAGGED_K && (g.gatherA || g.gatherB)) {
+      if constexpr (KRW == 8) {
+        tk = *(const CONST_AS i32x8*)(g.tokrow + kbeg + t * BK + KRW * wave);
+      } else {
+        const i32x4 v = *(const CONST_AS i32x4*)(g.tokrow + kbeg + t * BK + KRW * wave);
+        tk = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+      }
+    }
+    return tk;
+  };
+  auto issue = [&](int t, int st, const i32x8& tk) __attribute__((always_inline)) {
     const int k0 = t * BK;
     const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES;
     if constexpr (!RAGGED_K) {
@@ -263,16 +276,6 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
         dma16(src, bbase + (wave * QB + q) * 1024);
       }
     } else {
-      // token rows of the wave's KRW k rows, one scalar load
-      i32x8 tk = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (g.gatherA || g.gatherB) {
-        if constexpr (KRW == 8) {
-          tk = *(const CONST_AS i32x8*)(g.tokrow + kbeg + k0 + KRW * wave);
-        } else {
-          const i32x4 v = *(const CONST_AS i32x4*)(g.tokrow + kbeg + k0 + KRW * wave);
-          tk = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        }
-      }
       // Instruction q of an operand with C columns covers k rows KRW*wave + R*q + r, where
       // R = 512/C rows per instruction and r = lane / (C/8): the lane's token is one of R
       // elements at fixed positions (a two-way select for C = 256).  Selecting with fixed
@@ -366,8 +369,13 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   __syncthreads();  // s_slot / s_w visible; the arena is free
 #pragma unroll
   for (int t = 0; t < S - 1; ++t)
-    if (t < nk) issue(t, t);
+    if (t < nk) issue(t, t, load_tk(t));
   for (int it = 0; it < nk; ++it) {
+    // the tokens of the step refilled below are loaded before the wait, so the scalar load's
+    // latency overlaps the DMA wait and the barrier
+    const bool refill = it + S - 1 < nk;
+    i32x8 tk = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (RAGGED_K && refill) tk = load_tk(it + S - 1);
     const int pend = min(S - 2, nk - 1 - it);
     if (S >= 4 && pend >= 2) vm_wait_barrier<(S >= 4 ? 2 : 0) * DPT>();
     else if (S >= 3 && pend == 1) vm_wait_barrier<(S >= 3 ? 1 : 0) * DPT>();
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
         lds_barrier();
       }
     }
-    if (it + S - 1 < nk) issue(it + S - 1, (it + S - 1) % S);
+    if (refill) issue(it + S - 1, (it + S - 1) % S, tk);
     compute(it % S);
   }
 
