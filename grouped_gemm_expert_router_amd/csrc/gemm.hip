@@ -366,6 +366,9 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   // may stay in flight) and all waves are past tile t-1, refill tile t-1's stage with tile
   // t+S-1, then run tile t's MFMAs.
   const int nk = (klen + BK - 1) / BK;
+  // In an expert's last row tile, a wave whose rows all lie past the expert's end skips its
+  // fragment reads and MFMAs (uniform: mrows and wm are); it still issues its DMA share.
+  const bool busy = __builtin_amdgcn_readfirstlane(wm * TM < mrows);
   __syncthreads();  // s_slot / s_w visible; the arena is free
 #pragma unroll
   for (int t = 0; t < S - 1; ++t)
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
       }
     }
     if (refill) issue(it + S - 1, (it + S - 1) % S, tk);
-    compute(it % S);
+    if (busy) compute(it % S);
   }
 
   // ------------------------------------------------------------------ epilogues

@@ -198,6 +198,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   // One K stage = one 128-wide scale block: per 32-row fragment i, two 64-deep MFMAs per B
   // fragment into a temporary, then acc += temp * s_a(row) * s_b(block).  Row-fragment-major
   // order keeps only FN temporaries live next to the accumulators.
+  // In an expert's last row tile, a wave whose rows all lie past the expert's end skips its
+  // fragment reads and MFMAs (uniform: mrows and wm are); it still issues its DMA share.
+  const bool busy = __builtin_amdgcn_readfirstlane(wm * TM < mrows);
   auto compute = [&](int st, int kb) __attribute__((always_inline)) {
     const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, sbase = bbase + B_BYTES;
     i32x8 bv[2][FN];
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   for (int it = 0; it < nk; ++it) {
     vm_lgkm_wait_barrier<0>();
     if (it + 1 < nk) issue(it + 1, (it + 1) % S);
-    compute(it % S, it);
+    if (busy) compute(it % S, it);
   }
   __syncthreads();
 

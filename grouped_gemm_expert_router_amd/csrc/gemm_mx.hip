@@ -255,12 +255,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
 
   // ------------------------------------------------------------------ main loop (2 stages)
   const int nk = g.K / BK;
+  // In an expert's last row tile, a wave whose rows all lie past the expert's end skips its
+  // fragment reads and MFMAs (uniform: mrows and wm are); it still issues its DMA share.
+  const bool busy = __builtin_amdgcn_readfirstlane(wm * TM < mrows);
   __syncthreads();
   issue(0, 0);
   for (int it = 0; it < nk; ++it) {
     vm_lgkm_wait_barrier<0>();
     if (it + 1 < nk) issue(it + 1, (it + 1) % S);
-    compute(it % S);
+    if (busy) compute(it % S);
   }
   __syncthreads();
 
