@@ -91,7 +91,16 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
     const int64_t p = (int64_t)t * k + lane;
     const int pos = inv_perm[p];
     if (pos >= 0) {
-      for (int q = 0; q < nparts; ++q) dw += dwp[(int64_t)pos * nparts + q];
+      // partials summed in part order; loaded 4 at a time so the loads overlap
+      const float* src = dwp + (int64_t)pos * nparts;
+      for (int q0 = 0; q0 < nparts; q0 += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = q0 + u < nparts ? src[q0 + u] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (q0 + u < nparts) dw += v[u];
+      }
       wj = topk_w[p];
       if (ids) e = ids[p];
     }

@@ -79,8 +79,78 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
 }
 
+// G lanes per token (64/G tokens per wave), for k <= G.  Lane g holds logits g*EPL .. g*EPL+EPL-1
+// (one contiguous load).  Each of the k rounds takes the lane's best remaining (value, id), then
+// a butterfly over the G lanes on the same key (value descending, id ascending); every lane of
+// the group ends with the winner, lane j keeps slot j.  exp(v_j - v_0) is formed per round and
+// summed in slot order.
+template <int G, int EPL>
+__global__ __launch_bounds__(256) void router_topk_group_kernel(const float* __restrict__ logits, int T, int E,
+                                                                int k, int32_t* __restrict__ ids,
+                                                                float* __restrict__ w) {
+  const int gl = threadIdx.x % G;
+  const int t = (blockIdx.x * 256 + threadIdx.x) / G;
+  if (t >= T) return;  // uniform per group; a butterfly never leaves its group
+  const float* row = logits + (size_t)t * E;
+  float v[EPL];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = gl * EPL + i;
+    v[i] = e < E ? row[e] : 0.0f;
+    if (e < E) avail |= 1u << i;
+  }
+  float vmax = 0.0f, ssum = 0.0f, myz = 0.0f;
+  int mye = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.0f;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      // ids rise with i, so a tie keeps the earlier (lower) id
+      if (((avail >> i) & 1u) && (be == 0x7FFFFFFF || v[i] > bv)) {
+        bv = v[i];
+        be = gl * EPL + i;
+      }
+    }
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oe = __shfl_xor(be, m, 64);
+      // an empty candidate carries id 0x7FFFFFFF and loses to any real one
+      const bool take = (oe != 0x7FFFFFFF) && (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
+      if (take) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be / EPL == gl) avail &= ~(1u << (be % EPL));
+    if (j == 0) vmax = bv;
+    const float z = expf(bv - vmax);
+    ssum += z;
+    if (gl == j) {
+      myz = z;
+      mye = be;
+    }
+  }
+  if (gl < k) {
+    ids[(size_t)t * k + gl] = mye;
+    w[(size_t)t * k + gl] = myz / ssum;
+  }
+}
+
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st) {
   if (T == 0) return hipSuccess;
+  // group kernel: G lanes per token with EPL = 8 logits each, when k fits in the group
+  const unsigned gg16 = (unsigned)(((int64_t)T * 16 + 255) / 256);
+  if (E <= 64 && k <= 8) {
+    router_topk_group_kernel<8, 8><<<(unsigned)(((int64_t)T * 8 + 255) / 256), 256, 0, st>>>(logits, T, E, k, ids, w);
+    return hipGetLastError();
+  }
+  if (E <= 128 && k <= 16) {
+    router_topk_group_kernel<16, 8><<<gg16, 256, 0, st>>>(logits, T, E, k, ids, w);
+    return hipGetLastError();
+  }
   dim3 grid((T + 3) / 4), block(256);
   if (E <= 64)
     router_topk_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, w);
@@ -141,14 +211,32 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restri
   const int n = E * S;
   const int per = (n + 1023) / 1024;
   const int lo = threadIdx.x * per, hi = min(n, lo + per);
+  // the thread's entries are read in groups of 8 independent loads (one memory latency per
+  // group instead of one per entry)
+  constexpr int G = 8;
   int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += segcnt[i];
+  for (int i0 = lo; i0 < hi; i0 += G) {
+    int v[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) v[u] = i0 + u < hi ? segcnt[i0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < G; ++u) sum += v[u];
+  }
   int run;
   const int total = block_excl_scan_1024(sum, sh, &run);
-  for (int i = lo; i < hi; ++i) {
-    if (i % S == 0) first[i / S] = run;
-    segbase[i] = run;
-    run += segcnt[i];
+  for (int i0 = lo; i0 < hi; i0 += G) {
+    int v[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) v[u] = i0 + u < hi ? segcnt[i0 + u] : 0;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int i = i0 + u;
+      if (i < hi) {
+        if (i % S == 0) first[i / S] = run;
+        segbase[i] = run;
+        run += v[u];
+      }
+    }
   }
   if (S == 0)
     for (int e = threadIdx.x; e < E; e += 1024) first[e] = 0;

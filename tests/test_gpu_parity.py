@@ -40,6 +40,10 @@ CASES = {
     # more 256x256 output tiles than compute units in each ragged-M product (288 each), with
     # ragged row tails in every expert
     "tiles_beyond_one_per_cu": (4000, 768, 384, 8, 6, 16),
+    # router shapes: 16 lanes per token with k = 16 (every lane keeps a slot), and a row of 100
+    # logits that leaves some lanes partly or wholly without experts
+    "router_k16_E128": (100, 128, 128, 128, 16, 17),
+    "router_E100": (70, 128, 128, 100, 5, 18),
 }
 
 
@@ -78,13 +82,14 @@ def test_empty_experts_get_zero_weight_gradients():
     check_full_parity(gl, ref)
 
 
-def test_tie_heavy_routing_is_bitexact():
-    inp = _inputs(257, 128, 128, 32, 4, 22)
+@pytest.mark.parametrize("E,k", [(32, 4), (128, 8)])
+def test_tie_heavy_routing_is_bitexact(E, k):
+    inp = _inputs(257, 128, 128, E, k, 22)
     g = np.random.default_rng(0)
     L = g.integers(-2, 3, size=(inp.T, inp.E)).astype(np.float32)
     L[g.random(L.shape) < 0.2] = -0.0
     inp.logits = L
-    print("[case] tie-heavy routing", flush=True)
+    print(f"[case] tie-heavy routing E={E} k={k}", flush=True)
     gl = GpuLayer(inp).run()
     check_full_parity(gl, oracle_full(inp))
 
