@@ -202,39 +202,58 @@ __global__ __launch_bounds__(256) void plan_hist_kernel(const int32_t* __restric
     for (int e = lane; e < E; e += 64) segcnt[(size_t)e * S + s] = cnt[e];
 }
 
+// One block.  Thread t owns the contiguous (expert, segment) entries [t*per, (t+1)*per).  When the
+// table fits, it is moved through LDS with coalesced loads and stores (one CU issuing a scattered
+// 4-byte access per entry is limited by its request rate, not by latency); the LDS copy is padded
+// by one word per 16 so the threads' strided chunk walks hit distinct banks.
+constexpr int kScanLdsCap = 24576;
+__device__ __forceinline__ int scan_pad(int i) { return i + (i >> 4); }
+
 __global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restrict__ segcnt, int E, int S,
                                                          int32_t* __restrict__ segbase,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
   __shared__ int sh[64];
   __shared__ int first[1025];
+  __shared__ int buf[kScanLdsCap + kScanLdsCap / 16];
   const int n = E * S;
   const int per = (n + 1023) / 1024;
   const int lo = threadIdx.x * per, hi = min(n, lo + per);
-  // the thread's entries are read in groups of 8 independent loads (one memory latency per
-  // group instead of one per entry)
+  const bool in_lds = n <= kScanLdsCap;
+  if (in_lds) {
+    for (int i = threadIdx.x; i < n; i += 1024) buf[scan_pad(i)] = segcnt[i];
+    __syncthreads();
+  }
+  // out of LDS: the thread's entries are read in groups of 8 independent loads
   constexpr int G = 8;
   int sum = 0;
   for (int i0 = lo; i0 < hi; i0 += G) {
     int v[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) v[u] = i0 + u < hi ? segcnt[i0 + u] : 0;
+    for (int u = 0; u < G; ++u) v[u] = i0 + u < hi ? (in_lds ? buf[scan_pad(i0 + u)] : segcnt[i0 + u]) : 0;
 #pragma unroll
     for (int u = 0; u < G; ++u) sum += v[u];
   }
   int run;
   const int total = block_excl_scan_1024(sum, sh, &run);
+  // (expert, segment) of entry lo, then stepped along without a division per entry
+  int ce = S > 0 ? lo / S : 0, cs = S > 0 ? lo - ce * S : 0;
   for (int i0 = lo; i0 < hi; i0 += G) {
     int v[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) v[u] = i0 + u < hi ? segcnt[i0 + u] : 0;
+    for (int u = 0; u < G; ++u) v[u] = i0 + u < hi ? (in_lds ? buf[scan_pad(i0 + u)] : segcnt[i0 + u]) : 0;
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int i = i0 + u;
       if (i < hi) {
-        if (i % S == 0) first[i / S] = run;
-        segbase[i] = run;
+        if (cs == 0) first[ce] = run;
+        if (in_lds) buf[scan_pad(i)] = run;  // the thread's own entry: read above, no other reader
+        else segbase[i] = run;
         run += v[u];
+        if (++cs == S) {
+          cs = 0;
+          ++ce;
+        }
       }
     }
   }
@@ -242,6 +261,8 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restri
     for (int e = threadIdx.x; e < E; e += 1024) first[e] = 0;
   if (threadIdx.x == 0) first[E] = total;
   __syncthreads();
+  if (in_lds)
+    for (int i = threadIdx.x; i < n; i += 1024) segbase[i] = buf[scan_pad(i)];
   for (int e = threadIdx.x; e < E; e += 1024) {
     offsets[e] = first[e];
     counts[e] = first[e + 1] - first[e];
