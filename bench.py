@@ -366,7 +366,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.load_library()
     t_gen = time.perf_counter()
-    inp = make_config(args.config)
+    # the tiny workload is defined forward-only; a step here is forward + backward, so it gets an
+    # upstream gradient too (a smoke-sized run of the bench itself)
+    inp = make_config(args.config, fwd_only=False) if args.config == "tiny" else make_config(args.config)
     log(f"[bench] generated {args.config} inputs in {time.perf_counter() - t_gen:.1f}s; kernel sources "
         f"{kernel_source_hash()}")
     fp8 = inp.dtype == "fp8"
