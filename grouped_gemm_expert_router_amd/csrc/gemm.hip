@@ -151,7 +151,10 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     e = up[2 * u];
     kchunk = up[2 * u + 1];
     const int t = pos % per_u, nM = g.Mo / BM;
-    if (nM % 8 == 0 || nN % 8 != 0) {
+    // Within a unit, the tile index walks the dimension with fewer tiles first, so the tiles that
+    // run together cover all of it and share the other operand's rows in L2 (measured: qwen3 dW1
+    // and dW2 -2 %, Mixtral dW2 -5 % against walking by tile-count divisibility).
+    if (nM <= nN) {
       m0 = (t % nM) * BM;
       nt = t / nM;
     } else {
