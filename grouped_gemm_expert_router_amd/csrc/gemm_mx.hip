@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
   const int G_valid = *(const CONST_AS int32_t*)g.ntiles * nN;
   if ((int)blockIdx.x >= G_valid) return;
   const int lid = xcd_remap(blockIdx.x, G_valid);
-  const int2 rc = grouped_tile(lid, G_valid / nN, nN, MX_GM);
+  const int2 rc = grouped_tile(lid, G_valid / nN, nN, nN < 8 ? 1 : MX_GM);
   const int nt = rc.y;
   const int2 te = g.tiles[rc.x];
   const int e = te.x;
