@@ -36,6 +36,8 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* inv_perm, int T, int
 }
 
 // y[t] = bf16( sum_{j=0..k-1, inv_perm[t*k+j] >= 0} op[t*k+j] ) with an fp32 running sum.
+// The slots are taken 4 at a time: their row loads are all issued before the first add, and
+// the adds then run in slot order.  The per-pair rows are read once (non-temporal loads).
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ op,
                                                       const int32_t* __restrict__ inv_perm, int d, int k,
                                                       uint16_t* __restrict__ y) {
@@ -45,17 +47,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     float a[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) a[q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      if (inv_perm[p0 + j] < 0) continue;
-      const uint4 v = ((const uint4*)(op + (p0 + j) * d))[c];
-      a[0] += lo_bf16(v.x);
-      a[1] += hi_bf16(v.x);
-      a[2] += lo_bf16(v.y);
-      a[3] += hi_bf16(v.y);
-      a[4] += lo_bf16(v.z);
-      a[5] += hi_bf16(v.z);
-      a[6] += lo_bf16(v.w);
-      a[7] += hi_bf16(v.w);
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      uint4 v[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u;
+        ok[u] = j < k && inv_perm[p0 + j] >= 0;
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (ok[u]) {
+          v[u] = load_once16((const uint4*)(op + (p0 + j) * d) + c);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!ok[u]) continue;
+        a[0] += lo_bf16(v[u].x);
+        a[1] += hi_bf16(v[u].x);
+        a[2] += lo_bf16(v[u].y);
+        a[3] += hi_bf16(v[u].y);
+        a[4] += lo_bf16(v[u].z);
+        a[5] += hi_bf16(v[u].z);
+        a[6] += lo_bf16(v[u].w);
+        a[7] += hi_bf16(v[u].w);
+      }
     }
     uint4 o;
     o.x = pack_bf16x2(a[0], a[1]);

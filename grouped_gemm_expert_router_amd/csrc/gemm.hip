@@ -473,7 +473,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
       const uint16_t* hrow = g.Hs + pos * g.ldh + n0 + b_row(j) + 8 * h;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        hg[j][c] = *(const uint4*)(hrow + 16 * c);
+        hg[j][c] = *(const uint4*)(hrow + 16 * c);  // cached: the block's other loads share these lines
         hu[j][c] = *(const uint4*)(hrow + g.f + 16 * c);
       }
     };

@@ -510,7 +510,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-value group per thread
   const bool ok = i < n8;
   const int64_t ii = ok ? i : 0;
-  const uint4 v = *(const uint4*)(src + ii * 8);
+  const uint4 v = load_once16(src + ii * 8);
   float f[8] = {lo_bf16(v.x), hi_bf16(v.x), lo_bf16(v.y), hi_bf16(v.y),
                 lo_bf16(v.z), hi_bf16(v.z), lo_bf16(v.w), hi_bf16(v.w)};
   float sc;

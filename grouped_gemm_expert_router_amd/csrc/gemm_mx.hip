@@ -802,7 +802,7 @@ __global__ __launch_bounds__(256) void mx_quant_tokens_onepass_kernel(const uint
   for (int r = 0; r < 32; ++r) {
     const int64_t row = s_row[r];
     raw[r] = make_uint4(0u, 0u, 0u, 0u);
-    if (row >= 0) raw[r] = *(const uint4*)(src + row * C + c0);
+    if (row >= 0) raw[r] = load_once16(src + row * C + c0);
   }
   auto decode = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
     const uint4 w = raw[r];
