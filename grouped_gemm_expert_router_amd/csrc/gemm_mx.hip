@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __re
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool ok = i < n8;
   const int64_t ii = ok ? i : 0;
-  const uint4 v = *(const uint4*)(src + ii * 8);
+  const uint4 v = load_once16(src + ii * 8);
   float f[8] = {lo_bf16(v.x), hi_bf16(v.x), lo_bf16(v.y), hi_bf16(v.y),
                 lo_bf16(v.z), hi_bf16(v.z), lo_bf16(v.w), hi_bf16(v.w)};
   uint32_t ex;
@@ -802,7 +802,8 @@ __global__ __launch_bounds__(256) void mx_quant_tokens_onepass_kernel(const uint
   for (int r = 0; r < 32; ++r) {
     const int64_t row = s_row[r];
     raw[r] = make_uint4(0u, 0u, 0u, 0u);
-    if (row >= 0) raw[r] = load_once16(src + row * C + c0);
+    // a gathered token row is read again by its other experts' blocks: keep it cached then
+    if (row >= 0) raw[r] = gather ? *(const uint4*)(src + row * C + c0) : load_once16(src + row * C + c0);
   }
   auto decode = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
     const uint4 w = raw[r];
