@@ -34,6 +34,10 @@ __device__ __forceinline__ uint4 load_once16(const void* p) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+__device__ __forceinline__ void store_once16(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4_nt{v.x, v.y, v.z, v.w}, (u32x4_nt*)p);
+}
+
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
