@@ -54,11 +54,11 @@ STAGE_KERNEL_BF16 = {"gemm_up": "moe::grouped_gemm_kernel<0,", "gemm_down": "moe
                      "dlogits": "moe::dlogits_kernel", "wg_reduce": "moe::wg_reduce_kernel",
                      "plan": "moe::plan_", "tile_map": "moe::tile_map_kernel", "wg_split": "moe::wg_split_kernel",
                      "tokrow": "moe::tokrow_kernel", "permute": "moe::permute_kernel"}
+# blockwise fp8: the four data GEMMs in e4m3, the weight gradients in bf16 on x dequantised to bf16
 STAGE_KERNEL_FP8 = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_fp8_kernel<0>",
                         gemm_down="moe::grouped_gemm_fp8_kernel<1>", gemm_dact="moe::grouped_gemm_fp8_kernel<2>",
-                        gemm_dx="moe::grouped_gemm_fp8_kernel<3>", gemm_dw2="moe::grouped_gemm_mx_wg_kernel<0>",
-                        gemm_dw1="moe::grouped_gemm_mx_wg_kernel<1>", quant_dy="moe::quant_rows_kernel",
-                        mx_quant_t="moe::mx_quant_tokens", mx_pad="moe::mx_pad_offsets")
+                        gemm_dx="moe::grouped_gemm_fp8_kernel<3>", quant_dy="moe::quant_rows_kernel",
+                        dequant_x="moe::dequant_rows_kernel")
 FP8_STAGES = ("gemm_up", "gemm_down", "gemm_dact", "gemm_dx")
 
 
@@ -85,8 +85,11 @@ def is_fp8(config):
 
 
 def stage_dtype(config, stage):
-    # both fp8 formats run every GEMM in fp8, the weight gradients as MXFP8
-    return "fp8" if (is_fp8(config) and stage in MX_FP8_STAGES) else "bf16"
+    # MXFP8 runs every GEMM in fp8 (the weight gradients too); blockwise fp8 runs the four data
+    # GEMMs in fp8 and the weight gradients in bf16
+    if config.endswith(":mxfp8"):
+        return "fp8" if stage in MX_FP8_STAGES else "bf16"
+    return "fp8" if (is_fp8(config) and stage in FP8_STAGES) else "bf16"
 
 
 def stage_kernels(config):
@@ -95,7 +98,7 @@ def stage_kernels(config):
     return STAGE_KERNEL_FP8 if is_fp8(config) else STAGE_KERNEL_BF16
 
 
-def stage_bytes(stage, T, d, f, E, k, A, fp8_in=False):
+def stage_bytes(stage, T, d, f, E, k, A):
     """Algorithmic HBM bytes of one launch of a bandwidth-bound stage (each byte the stage
     must read or write once; A = routed pairs)."""
     if stage in ("combine", "combine_dx"):
@@ -108,6 +111,8 @@ def stage_bytes(stage, T, d, f, E, k, A, fp8_in=False):
         return T * k * 4 * 3 + T * E * 4
     if stage == "quant_dy":
         return T * d * 2 + T * d + T * (d // 128) * 4
+    if stage == "dequant_x":                                 # e4m3 + 1x128 scales in, bf16 out
+        return T * d + T * (d // 128) * 4 + T * d * 2
     if stage in ("mx_quant_x", "mx_quant_dy"):
         return T * d * 2 + T * d + T * d // 32
     if stage == "mx_quant_as_t":                            # sorted rows in, token-axis blocks out
@@ -115,7 +120,7 @@ def stage_bytes(stage, T, d, f, E, k, A, fp8_in=False):
     if stage == "mx_quant_dh_t":
         return A * 2 * f * 2 + A * 2 * f + A * 2 * f // 32
     if stage in ("mx_quant_x_t", "mx_quant_dy_t"):           # each token row read once, A rows out
-        return T * d * (1 if (stage == "mx_quant_x_t" and fp8_in) else 2) + A * d + A * d // 32
+        return T * d * 2 + A * d + A * d // 32
     if stage in ("mx_quant_w1", "mx_quant_w2"):
         return E * d * f * (2 + 1) + E * d * f // 32     # one of W1 (2df) / W2 (df): bytes of W1 halved
     return None
@@ -160,11 +165,12 @@ def stored_traffic(config, stage):
 
 # ------------------------------------------------------------------ CPU oracle baseline
 def _host_cores():
+    """Host cores this process may run on (its CPU affinity), all of which the oracle's BLAS uses."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, n)
 
 
 def _cpu_model():
@@ -224,6 +230,7 @@ def cpu_baseline(inp, target_s: float):
                 break
             n = int(min(inp.T, max(2 * n, n * target_s / max(dt, 1e-3))))
     return {"value": 18.0 * pairs * inp.d * inp.f / dt / 1e12, "unit": "TFLOPS", "cores": int(threads),
+            "affinity_cores": ncores, "blas_threads": int(threads),
             "kind": "oracle", "tokens_per_s": n / dt, "seconds": dt, "cpu_model": _cpu_model(),
             "sample": f"first {n} of {inp.T} tokens of the same workload ({pairs} routed pairs, all {inp.E} "
                       f"experts), {'plan' if fp8 else 'route+plan'}+forward+backward in fp64 numpy on "
@@ -479,7 +486,7 @@ def main():
             ent["frac_mfma_peak"] = ent["tflops"] / pk
             ideal_ms += fl / (pk * 1e12) * 1e3
         else:
-            by = stage_bytes(stage, T, d, f, E, k, A, fp8_in=fp8)
+            by = stage_bytes(stage, T, d, f, E, k, A)
             if by:
                 ent["gbs"] = by / (avg * 1e-3) / 1e9
         stages[stage] = ent
@@ -496,7 +503,7 @@ def main():
                 "frac": achieved / pk, "traffic": traffic, "dtype": stage_dtype(run_name, dom),
                 "algorithmic_flop_per_launch": fl, "avg_launch_ms": dom_e["avg_ms"]}
     else:
-        by = stage_bytes(dom, T, d, f, E, k, A, fp8_in=fp8)
+        by = stage_bytes(dom, T, d, f, E, k, A)
         achieved = by / (dom_e["avg_ms"] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": by,

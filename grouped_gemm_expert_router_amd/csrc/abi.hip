@@ -32,8 +32,8 @@ int check_dims(const moe_dims* d) {
   const int bm = d->dtype != MOE_BF16 ? kFp8BM : kGemmBM;
   const int64_t rows = (A + bm - 1) / bm + (A < d->E ? A : d->E);
   if (rows * (d->f / 64 > d->d / 128 ? d->f / 64 : d->d / 128) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
-  // the fp8 weight gradients index the 128-padded expert segments with 32-bit rows
-  if (d->dtype != MOE_BF16 && mx_padded_rows(A, (int)d->E) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  // the MXFP8 weight gradients index the 128-padded expert segments with 32-bit rows
+  if (d->dtype == MOE_MXFP8 && mx_padded_rows(A, (int)d->E) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -49,8 +49,8 @@ MoeShape shape_of(const moe_dims* d) {
   return MoeShape{(int)d->T, (int)d->d, (int)d->f, (int)d->E, (int)d->k};
 }
 
-// fp8: asq/ass (As in e4m3 + scales); dyq/dys, dHq/dHs; poff and tqa/tea, tqb/teb as for MXFP8
-// below (the weight gradients run as MXFP8 in both fp8 formats).
+// fp8: asq/ass (As in e4m3 + scales); dyq/dys, dHq/dHs; xbf (x dequantised to bf16 for the
+// bf16 weight gradients).
 // MXFP8 (codes + E8M0 exponents): asq/ass; xq/xe, w1q/w1e and w2q/w2e (forward quantisation of
 // x, W1 and W2); dyq/dys, dHq/dHs, w1q/w1e and w2q/w2e (W1, W2 along the data gradients' K);
 // for the weight gradients poff (padded expert offsets) and tqa/tea, tqb/teb (the two operands
@@ -59,7 +59,7 @@ struct FwdLayout {
   size_t tiles, ntiles, op, asq, ass, xq, xe, w1q, w1e, w2q, w2e, total;
 };
 struct BwdLayout {
-  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dHq, dHs, w1q,
+  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dHq, dHs, xbf, w1q,
       w1e, w2q, w2e, poff, tqa, tea, tqb, teb, total;
   int max_partials;
 };
@@ -142,6 +142,8 @@ BwdLayout bwd_layout(const moe_dims* d) {
     off += al256((size_t)A * 2 * d->f);
     L.dHs = off;
     off += al256((size_t)A * (2 * d->f / 128) * sizeof(float));
+    L.xbf = off;
+    off += al256((size_t)d->T * d->d * 2);
   }
   if (is_mx(d)) {
     const size_t dd = d->d, ff = d->f, T = d->T;
@@ -153,9 +155,7 @@ BwdLayout bwd_layout(const moe_dims* d) {
     off += al256((size_t)A * 2 * ff);
     L.dHs = off;
     off += al256((size_t)A * (2 * ff / 32));
-  }
-  if (is_fp8(d) || is_mx(d)) {
-    const size_t E = d->E, dd = d->d, ff = d->f;
+    const size_t E = d->E;
     const size_t P = (size_t)mx_padded_rows(A, (int)E);
     const size_t ca = ff > dd ? ff : dd, cb = dd > 2 * ff ? dd : 2 * ff;  // As or x; dy or dH
     L.poff = off;
@@ -346,24 +346,23 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
   return MOE_OK;
 }
 
-// MXFP8 weight gradients (both fp8 formats): dW2 = As^T dy and dW1 = x^T dH with every operand
-// quantised along the token axis in 32-row blocks inside each expert's 128-padded segment.  x is
-// bf16, or e4m3 codes with 1x128 scales (x8, x8s).
-static int mx_weight_grads(const MoeShape& s, const BwdLayout& L, char* w, const uint16_t* x, const uint8_t* x8,
-                    const float* x8s, const uint16_t* dy, const uint16_t* As, const uint16_t* dH,
-                    const int32_t* offsets, const int32_t* perm, uint16_t* dW1, uint16_t* dW2, hipStream_t st) {
+// MXFP8 weight gradients: dW2 = As^T dy and dW1 = x^T dH with every operand quantised along the
+// token axis in 32-row blocks inside each expert's 128-padded segment.
+static int mx_weight_grads(const MoeShape& s, const BwdLayout& L, char* w, const uint16_t* x, const uint16_t* dy,
+                           const uint16_t* As, const uint16_t* dH, const int32_t* offsets, const int32_t* perm,
+                           uint16_t* dW1, uint16_t* dW2, hipStream_t st) {
   int32_t* poff = (int32_t*)(w + L.poff);
   uint8_t *tqa = (uint8_t*)(w + L.tqa), *tea = (uint8_t*)(w + L.tea);
   uint8_t *tqb = (uint8_t*)(w + L.tqb), *teb = (uint8_t*)(w + L.teb);
   const WgSplit spm = wg_split_of(L, w, poff);
   MOE_TRY("mx_pad", launch_mx_pad_offsets(offsets, s.E, poff, st));
   MOE_TRY("wg_split", launch_wg_split(s, poff, spm, st));
-  MOE_TRY("mx_quant_as_t", launch_mx_quant_tokens(As, nullptr, nullptr, s.f, 0, s, offsets, perm, poff, tqa, tea, st));
-  MOE_TRY("mx_quant_dy_t", launch_mx_quant_tokens(dy, nullptr, nullptr, s.d, 1, s, offsets, perm, poff, tqb, teb, st));
+  MOE_TRY("mx_quant_as_t", launch_mx_quant_tokens(As, s.f, 0, s, offsets, perm, poff, tqa, tea, st));
+  MOE_TRY("mx_quant_dy_t", launch_mx_quant_tokens(dy, s.d, 1, s, offsets, perm, poff, tqb, teb, st));
   MOE_TRY("gemm_dw2", launch_mx_wg(0, s, tqa, tea, s.f, tqb, teb, s.d, poff, spm, dW2, st));
   MOE_TRY("wg_reduce", launch_wg_reduce(s, spm, (int64_t)s.f * s.d, dW2, st));
-  MOE_TRY("mx_quant_x_t", launch_mx_quant_tokens(x, x8, x8s, s.d, 1, s, offsets, perm, poff, tqa, tea, st));
-  MOE_TRY("mx_quant_dh_t", launch_mx_quant_tokens(dH, nullptr, nullptr, 2 * s.f, 0, s, offsets, perm, poff, tqb, teb, st));
+  MOE_TRY("mx_quant_x_t", launch_mx_quant_tokens(x, s.d, 1, s, offsets, perm, poff, tqa, tea, st));
+  MOE_TRY("mx_quant_dh_t", launch_mx_quant_tokens(dH, 2 * s.f, 0, s, offsets, perm, poff, tqb, teb, st));
   MOE_TRY("gemm_dw1", launch_mx_wg(1, s, tqa, tea, s.d, tqb, teb, 2 * s.f, poff, spm, dW1, st));
   MOE_TRY("wg_reduce", launch_wg_reduce(s, spm, (int64_t)s.d * 2 * s.f, dW1, st));
   return MOE_OK;
@@ -429,8 +428,8 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                                         dwp, st));
     MOE_TRY("gemm_dx", launch_mx_dx(s, dHq, dHe, w1q, w1e, offsets, perm, tiles, ntiles, dXp, st));
     MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
-    rc = mx_weight_grads(s, L, w, (const uint16_t*)x, nullptr, nullptr, (const uint16_t*)dy, As, dH, offsets, perm,
-                         (uint16_t*)dW1, (uint16_t*)dW2, st);
+    rc = mx_weight_grads(s, L, w, (const uint16_t*)x, (const uint16_t*)dy, As, dH, offsets, perm, (uint16_t*)dW1,
+                         (uint16_t*)dW2, st);
     if (rc) return rc;
     MOE_TRY("dlogits", launch_dlogits(dwp, dact_parts(dims), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w,
                                       d_logits, st));
@@ -448,9 +447,15 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                                          dHs, dwp, st));
     MOE_TRY("gemm_dx", launch_fp8_dx(s, dHq, dHs, W18, W1_scale, offsets, perm, tiles, ntiles, dXp, st));
     MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));
-    rc = mx_weight_grads(s, L, w, nullptr, (const uint8_t*)x, x_scale, (const uint16_t*)dy, As, dH, offsets, perm,
-                         (uint16_t*)dW1, (uint16_t*)dW2, st);
-    if (rc) return rc;
+    // weight gradients in bf16 MFMA: x dequantised to bf16 once, with dy, As and dH as they are
+    uint16_t* xbf = (uint16_t*)(w + L.xbf);
+    MOE_TRY("dequant_x", launch_dequant_rows((const uint8_t*)x, x_scale, s.T, s.d, xbf, st));
+    MOE_TRY("tokrow", launch_tokrow(perm, offsets, s.E, (int64_t)s.T * s.k, s.k, tokrow, st));
+    MOE_TRY("wg_split", launch_wg_split(s, offsets, sp, st));
+    MOE_TRY("gemm_dw2", launch_gemm_dw2(s, As, (const uint16_t*)dy, offsets, perm, tokrow, sp, (uint16_t*)dW2, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.f * s.d, (uint16_t*)dW2, st));
+    MOE_TRY("gemm_dw1", launch_gemm_dw1(s, xbf, dH, offsets, perm, tokrow, sp, (uint16_t*)dW1, st));
+    MOE_TRY("wg_reduce", launch_wg_reduce(s, sp, (int64_t)s.d * 2 * s.f, (uint16_t*)dW1, st));
     MOE_TRY("dlogits", launch_dlogits(dwp, dact_parts(dims), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w,
                                       d_logits, st));
     return MOE_OK;
@@ -489,6 +494,7 @@ int moe_combine(const moe_dims* dims, const void* op, const int32_t* inv_perm, v
   int rc = check_dims(dims);
   if (rc) return rc;
   if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (dims->T == 0) return MOE_OK;  // an empty layer has nothing to combine
   if (!op || !inv_perm || !y) return MOE_ERR_NULL;
   if (!al16(op) || !al16(y)) return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;

@@ -531,4 +531,33 @@ hipError_t launch_quant_rows(const uint16_t* src, int64_t rows, int cols, uint8_
   return hipGetLastError();
 }
 
+// e4m3 codes with one fp32 scale per row per 128 values -> bf16 (code * scale in fp32, one RNE
+// rounding).  One thread per 8 values: an 8-byte load, a 16-byte store.
+__global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__ qs,
+                                                           int64_t n8, int cols, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t e0 = i * 8, row = e0 / cols;
+  const float sc = qs[row * (cols / 128) + (e0 % cols) / 128];  // the 8 values share one 128-block
+  const u32x2 w = *(const u32x2*)(q + e0);
+  uint32_t o[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t word = h ? w.y : w.x;
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+    o[2 * h] = pack_bf16x2(a[0] * sc, a[1] * sc);
+    o[2 * h + 1] = pack_bf16x2(b[0] * sc, b[1] * sc);
+  }
+  *(uint4*)(out + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, int cols, uint16_t* out,
+                               hipStream_t st) {
+  const int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipSuccess;
+  dequant_rows_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(q, qs, n8, cols, out);
+  return hipGetLastError();
+}
+
 }  // namespace moe

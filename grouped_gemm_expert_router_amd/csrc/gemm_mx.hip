@@ -679,8 +679,7 @@ __global__ __launch_bounds__(1024) void mx_pad_offsets_kernel(const int32_t* __r
 
 // Rows of a source [*, C] in the experts' sorted order -- row perm[pos] / kslots of a
 // token-major source when gather, else row pos -- quantised along the rows into the padded
-// segments: codes [P, C], exponents [P / 32, C].  The source is bf16, or (FP8SRC) e4m3 codes
-// with one fp32 scale per 128 values of a row, taken as code times scale in fp32.  One block per
+// segments: codes [P, C], exponents [P / 32, C].  The source is bf16.  One block per
 // 32 padded rows and 2048 columns; thread t owns 8 columns: a first pass over the 32 rows finds
 // their maxima, a second (from L2) writes the codes.  Rows past the expert's count are zero.
 // Source row of each of the 32 padded positions pp0.. (-1 for the zero rows that pad an expert's
@@ -707,10 +706,8 @@ __device__ __forceinline__ void token_block_rows(int pp0, int gather, int kslots
   __syncthreads();
 }
 
-template <bool FP8SRC>
-__global__ __launch_bounds__(256) void mx_quant_tokens_kernel(const void* __restrict__ src_, const float* __restrict__ ss,
-                                                              int C, int gather, int kslots,
-                                                              const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(256) void mx_quant_tokens_kernel(const uint16_t* __restrict__ src, int C, int gather,
+                                                              int kslots, const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ perm,
                                                               const int32_t* __restrict__ poff, int E,
                                                               uint8_t* __restrict__ q, uint8_t* __restrict__ qe) {
@@ -722,31 +719,10 @@ __global__ __launch_bounds__(256) void mx_quant_tokens_kernel(const void* __rest
   if (c0 >= C) return;                               // C is a multiple of 8
   auto load8 = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
     const int64_t row = s_row[r];
-    if constexpr (FP8SRC) {
-      const uint8_t* src = (const uint8_t*)src_;
-      u32x2 w = {0u, 0u};
-      float sc = 0.0f;
-      if (row >= 0) {
-        w = *(const u32x2*)(src + row * C + c0);
-        sc = ss[row * (C / 128) + c0 / 128];  // the 8 columns share one 128-block
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t word = h ? w.y : w.x;
-        const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-        const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-        v[4 * h] = a[0] * sc;
-        v[4 * h + 1] = a[1] * sc;
-        v[4 * h + 2] = b[0] * sc;
-        v[4 * h + 3] = b[1] * sc;
-      }
-    } else {
-      const uint16_t* src = (const uint16_t*)src_;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (row >= 0) w = *(const uint4*)(src + row * C + c0);
-      v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x); v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
-      v[4] = lo_bf16(w.z); v[5] = hi_bf16(w.z); v[6] = lo_bf16(w.w); v[7] = hi_bf16(w.w);
-    }
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (row >= 0) w = *(const uint4*)(src + row * C + c0);
+    v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x); v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
+    v[4] = lo_bf16(w.z); v[5] = hi_bf16(w.z); v[6] = lo_bf16(w.w); v[7] = hi_bf16(w.w);
   };
   float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll 8
@@ -782,8 +758,8 @@ __global__ __launch_bounds__(256) void mx_quant_tokens_kernel(const void* __rest
 
 // The same quantisation for wide bf16 sources (C >= 1024) in one read: each thread issues the
 // loads of its 32 rows up front and keeps the raw words in registers for both the column maxima
-// and the codes (the two-pass form re-reads the rows from L2 for the codes).  Narrow sources and
-// e4m3 sources keep the two-pass form, which measured faster for them.
+// and the codes (the two-pass form re-reads the rows from L2 for the codes).  Narrow sources keep
+// the two-pass form, which measured faster for them.
 __global__ __launch_bounds__(256) void mx_quant_tokens_onepass_kernel(const uint16_t* __restrict__ src, int C,
                                                                       int gather, int kslots,
                                                                       const int32_t* __restrict__ offsets,
@@ -1051,18 +1027,15 @@ hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* poff, h
   return hipGetLastError();
 }
 
-hipError_t launch_mx_quant_tokens(const uint16_t* src, const uint8_t* src8, const float* src8_scale, int C,
-                                  int gather, const MoeShape& s, const int32_t* offsets, const int32_t* perm,
-                                  const int32_t* poff, uint8_t* q, uint8_t* qe, hipStream_t st) {
+hipError_t launch_mx_quant_tokens(const uint16_t* src, int C, int gather, const MoeShape& s, const int32_t* offsets,
+                                  const int32_t* perm, const int32_t* poff, uint8_t* q, uint8_t* qe, hipStream_t st) {
   const int64_t blocks = mx_padded_rows((int64_t)s.T * s.k, s.E) / 32;
   if (blocks == 0) return hipSuccess;
   dim3 grid((unsigned)blocks, (unsigned)((C + 2047) / 2048));
-  if (src8)
-    mx_quant_tokens_kernel<true><<<grid, 256, 0, st>>>(src8, src8_scale, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
-  else if (C >= 1024)
+  if (C >= 1024)
     mx_quant_tokens_onepass_kernel<<<grid, 256, 0, st>>>(src, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
   else
-    mx_quant_tokens_kernel<false><<<grid, 256, 0, st>>>(src, nullptr, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
+    mx_quant_tokens_kernel<<<grid, 256, 0, st>>>(src, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
   return hipGetLastError();
 }
 

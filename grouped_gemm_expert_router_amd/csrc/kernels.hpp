@@ -95,6 +95,8 @@ hipError_t launch_fp8_dx(const MoeShape& s, const uint8_t* dHq, const float* dHs
                          uint16_t* dXp, hipStream_t st);
 // bf16 rows -> e4m3 + one scale per row per 128 values (cols % 128 == 0), and back to bf16.
 hipError_t launch_quant_rows(const uint16_t* src, int64_t rows, int cols, uint8_t* q, float* qs, hipStream_t st);
+hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, int cols, uint16_t* out,
+                               hipStream_t st);
 // MXFP8: e4m3 codes with one E8M0 exponent byte per 32 values along each GEMM's K.
 // along_rows = 0: blocks of 32 consecutive values of a row -> exponents [batch, rows, cols/32];
 // along_rows = 1: blocks of 32 consecutive rows of a column -> exponents [batch, rows/32, cols].
@@ -105,10 +107,10 @@ hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int col
 // MXFP8 weight gradients: each expert's rows padded to a multiple of 128 (see gemm_mx.hip).
 inline int64_t mx_padded_rows(int64_t A, int E) { return (A + 127 * (int64_t)E + 127) / 128 * 128; }
 hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
-// src bf16, or src8 e4m3 codes with src8_scale (one fp32 per 128 values of a row) when src8 is set
-hipError_t launch_mx_quant_tokens(const uint16_t* src, const uint8_t* src8, const float* src8_scale, int C,
-                                  int gather, const MoeShape& s, const int32_t* offsets, const int32_t* perm,
-                                  const int32_t* poff, uint8_t* q, uint8_t* qe, hipStream_t st);
+// bf16 rows (token rows perm[pos] / k when gather is set, else sorted rows pos) -> e4m3 codes in
+// blocks of 32 consecutive sorted rows of one expert, with E8M0 exponents
+hipError_t launch_mx_quant_tokens(const uint16_t* src, int C, int gather, const MoeShape& s, const int32_t* offsets,
+                                  const int32_t* perm, const int32_t* poff, uint8_t* q, uint8_t* qe, hipStream_t st);
 hipError_t launch_mx_wg(int which, const MoeShape& s, const uint8_t* Aq, const uint8_t* Ae, int Mo, const uint8_t* Bq,
                         const uint8_t* Be, int N, const int32_t* poff, const WgSplit& sp, uint16_t* dW,
                         hipStream_t st);

@@ -42,7 +42,7 @@
  *     a launch failed (moe_status_string() then names the HIP error).
  *   - Shapes (MOE_ERR_SHAPE otherwise): T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64),
  *     d and f positive multiples of 128 (MOE_FP8_E4M3, MOE_MXFP8: of 256) and at most 65536,
- *     T*k < 2^31 (MOE_FP8_E4M3, MOE_MXFP8: T*k + 127*E rounded up to 128 < 2^31).
+ *     T*k < 2^31 (MOE_MXFP8: T*k + 127*E rounded up to 128 < 2^31).
  *   - fp8 (MOE_FP8_E4M3): codes are OCP e4m3 (bias 7, max 448, no infinities); a block's value
  *     is code * scale with its fp32 scale ([Prime] "Mit csinált a Prime Intellect?": blockwise
  *     FP8 is one of the kernel's data types).  Outputs and gradients stay bf16/fp32.
@@ -139,12 +139,14 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale,
  * w[t,j] * (d_topk_w[t,j] - sum_i w[t,i] d_topk_w[t,i]) and 0 elsewhere (the softmax over the
  * kept logits; topk_ids is then required).  `saved` must come from moe_forward on the same
  * inputs.  Every reduction has a fixed order, so results are bitwise reproducible.
- * fp8: dy is quantised like the forward activations (1x128 blocks) for the two data-gradient
- * GEMMs and dH is requantised the same way between them.
- * Weight gradients, fp8 and MXFP8: dW2 = As^T dy and dW1 = x^T dH run as MXFP8 GEMMs whose K is
- * the expert's rows; both operands are quantised in blocks of 32 consecutive sorted rows that
- * never straddle two experts ([JAX] "Csoportosított mátrixszorzás és összevont adatmozgatás":
- * group-aware quantisation).  For MOE_FP8_E4M3, x enters as code * scale in fp32. */
+ * fp8 (MOE_FP8_E4M3): dy is quantised like the forward activations (1x128 blocks) for the two
+ * data-gradient GEMMs and dH is requantised the same way between them.  The weight gradients
+ * dW2 = As^T dy and dW1 = x^T dH run as bf16 GEMMs with fp32 accumulation on the bf16 dy, the
+ * layer's own bf16 As and dH, and x dequantised once to bf16 (code * scale in fp32, one
+ * rounding): their K is the token axis, which the 1x128 blocks of the inputs do not follow.
+ * MXFP8 (MOE_MXFP8): the weight gradients run as MXFP8 GEMMs whose K is the expert's rows; both
+ * operands are quantised in blocks of 32 consecutive sorted rows that never straddle two experts
+ * ([JAX] "Csoportosított mátrixszorzás és összevont adatmozgatás": group-aware quantisation). */
 int moe_backward(const moe_dims* dims, const void* dy, const void* x, const float* x_scale,
                  const void* W1, const float* W1_scale, const void* W2, const float* W2_scale,
                  const int32_t* topk_ids, const float* topk_w, const int32_t* offsets,
@@ -175,7 +177,6 @@ int moe_combine(const moe_dims* dims, const void* op, const int32_t* inv_perm, v
 typedef void (*moe_stage_hook)(const char* stage, int begin, void* stream, void* user);
 int moe_set_stage_hook(moe_stage_hook hook, void* user);
 
-/* Static string for a status code (for MOE_ERR_HIP: the last HIP error on this thread). */
 /* MXFP8 quantisation on its own (the same kernels the MOE_MXFP8 path runs).  src is bf16
  * [batch, rows, cols] (row-major).  block_axis = 1: each block is 32 consecutive values of a row
  * (cols % 32 == 0), exps is [batch, rows, cols/32]; block_axis = 0: each block is 32
@@ -186,6 +187,7 @@ int moe_set_stage_hook(moe_stage_hook hook, void* user);
 int moe_mxfp8_quantize(const void* src, int64_t batch, int64_t rows, int64_t cols, int block_axis, void* codes,
                        void* exps, void* stream);
 
+/* Static string for a status code (for MOE_ERR_HIP: the last HIP error on this thread). */
 const char* moe_status_string(int status);
 
 #ifdef __cplusplus

@@ -124,9 +124,16 @@ def oracle_full(inp):
     pl = oracle.plan(ids, inp.E)
     out = dict(ids=ids, w=w, plan=pl, y=oracle.forward(x, W1, W2, ids, w))
     if dy is not None:
-        # the fp8 layer runs its weight gradients as MXFP8 with token-axis blocks of x and dy
-        q_dw = oracle.mx_roundtrip_rows if inp.dtype == "fp8" else None
-        out.update(oracle.backward(x, W1, W2, ids, w, dy, logits_routed=inp.logits is not None, q_dw=q_dw))
+        out.update(oracle.backward(x, W1, W2, ids, w, dy, logits_routed=inp.logits is not None))
+    return out
+
+
+def summarize_errs(errs: dict) -> dict:
+    """Per-tensor maxima of an error dict (the per-expert dW entries folded into dW1, dW2)."""
+    out = {}
+    for k, v in errs.items():
+        name = k.split("[")[0]
+        out[name] = max(out.get(name, 0.0), v)
     return out
 
 

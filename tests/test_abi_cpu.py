@@ -74,11 +74,12 @@ def test_fp8_shape_rules(lib):
     assert sz(lib, moe.dims(64, 256, 384, 8, 2, dtype=moe.MOE_FP8_E4M3), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
     bf = moe.dims(64, 256, 256, 8, 2)
     f8 = moe.dims(64, 256, 256, 8, 2, dtype=moe.MOE_FP8_E4M3)
-    # fp8 adds the e4m3 copies of As (forward) and of dy, dH plus the token-axis operand buffers
-    # of the weight gradients (backward)
-    A, d, f = 128, 256, 256
+    # fp8 adds the e4m3 copies of As (forward) and of dy and dH, plus x dequantised to bf16 for the
+    # bf16 weight gradients (backward)
+    A, T, d, f = 128, 64, 256, 256
     assert sz(lib, f8, moe.MOE_WS_FORWARD)[1] >= sz(lib, bf, moe.MOE_WS_FORWARD)[1] + A * f + A * (f // 128) * 4
-    assert sz(lib, f8, moe.MOE_WS_BACKWARD)[1] >= sz(lib, bf, moe.MOE_WS_BACKWARD)[1] + 64 * d * 3 + A * 2 * f
+    assert sz(lib, f8, moe.MOE_WS_BACKWARD)[1] >= (sz(lib, bf, moe.MOE_WS_BACKWARD)[1] + T * d + A * 2 * f
+                                                   + T * d * 2)
 
 
 def test_workspace_sizes_scale_with_pairs_not_capacity(lib):
@@ -144,6 +145,11 @@ def test_forward_backward_argument_errors(lib):
     assert lib.moe_permute(ctypes.byref(dm), F, F, None, None) == moe.MOE_ERR_NULL
     assert lib.moe_permute(ctypes.byref(dm), F + 4, F, F, None) == moe.MOE_ERR_ALIGN
     assert lib.moe_combine(ctypes.byref(dm), F + 4, F, F, None) == moe.MOE_ERR_ALIGN
+    # an empty layer is legal with NULL buffers for the data-movement steps, as for the layer
+    empty = moe.dims(0, 128, 256, 8, 2)
+    assert lib.moe_combine(ctypes.byref(empty), None, None, None, None) == moe.MOE_OK
+    assert lib.moe_permute(ctypes.byref(empty), None, None, None, None) == moe.MOE_OK
+    assert lib.moe_forward(ctypes.byref(empty), *([None] * 13), 0, None) == moe.MOE_OK
 
 
 def test_mxfp8_argument_rules(lib):
@@ -167,11 +173,13 @@ def test_mxfp8_argument_rules(lib):
     assert q(F, 0, 64, 64, 1, None, None) == moe.MOE_OK         # empty input: nothing to do
 
 
-def test_fp8_padded_rows_rule(lib):
-    # T*k = 2^31 - 1000 pairs is a legal bf16 layer; the fp8 formats pad each expert's rows to a
-    # multiple of 128 for the weight gradients, which would pass 2^31 with 1024 experts
+def test_mxfp8_padded_rows_rule(lib):
+    # T*k = 2^31 - 1000 pairs is a legal bf16 (and blockwise fp8) layer; MXFP8 pads each expert's
+    # rows to a multiple of 128 for the weight gradients, which would pass 2^31 with 1024 experts
     T, k, E = 268435331, 8, 1024
     assert sz(lib, moe.dims(T, 256, 256, E, k), moe.MOE_WS_FORWARD)[0] == moe.MOE_OK
-    for dt in (moe.MOE_FP8_E4M3, moe.MOE_MXFP8):
-        assert sz(lib, moe.dims(T, 256, 256, E, k, dtype=dt), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
-        assert sz(lib, moe.dims(T // 2, 256, 256, E, k, dtype=dt), moe.MOE_WS_FORWARD)[0] == moe.MOE_OK
+    assert sz(lib, moe.dims(T, 256, 256, E, k, dtype=moe.MOE_FP8_E4M3), moe.MOE_WS_FORWARD)[0] == moe.MOE_OK
+    mx = moe.MOE_MXFP8
+    assert sz(lib, moe.dims(T, 256, 256, E, k, dtype=mx), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
+    assert sz(lib, moe.dims(T // 2, 256, 256, E, k, dtype=mx), moe.MOE_WS_FORWARD)[0] == moe.MOE_OK
+

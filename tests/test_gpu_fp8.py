@@ -1,7 +1,7 @@
 """GPU parity of the blockwise-fp8 path (OCP e4m3 operands with fp32 scales per 1x128 block of
-activations and per 128x128 block of weights, bf16 outputs) against the fp64 oracle run on the
-exactly dequantised inputs.  The weight gradients run as MXFP8 with x and dy in blocks of 32 rows
-along the token axis inside each expert, which the oracle models (As and dH stay exact in it).
+activations and per 128x128 block of weights, bf16 outputs) against the plain fp64 oracle run on
+the exactly dequantised inputs and the bf16 dy, for every output including the weight gradients
+(the layer runs those in bf16 on x dequantised to bf16).
 
 Inputs are one rank's share of an expert-parallel layer, already routed (expert id -1 marks a
 slot that another rank serves).  Small cases compare every output element; the DeepSeek-V3
@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from workloads import make_config, make_prerouted_fp8
-from moe_testlib import GpuLayer, TOL_FP8, check_full_parity, oracle_full, rel_err, to_np
+from moe_testlib import GpuLayer, TOL_FP8, check_full_parity, oracle_full, rel_err, summarize_errs, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def test_fp8_layer_parity(name):
     print(f"[case] {name} T={inp.T} d={d} f={f} E={E} k={k} counts={counts.tolist()}", flush=True)
     gl = GpuLayer(inp).run()
     errs = check_full_parity(gl, oracle_full(inp), tol=TOL_FP8)
-    print(f"[case] {name}: max err {max(errs.values()):.2e}", flush=True)
+    print(f"[case] {name}: " + ", ".join(f"{k}={v:.2e}" for k, v in summarize_errs(errs).items()), flush=True)
 
 
 def test_fp8_no_local_tokens():
@@ -50,14 +50,6 @@ def test_fp8_no_local_tokens():
     gl.run()
     assert torch.all(gl.b["offsets"] == 0)
     assert torch.all(gl.b["dW1"] == 0) and torch.all(gl.b["dW2"] == 0)
-
-
-def test_fp8_sparse_case_has_empty_experts():
-    # the sparse case exercises experts that receive no token (zero weight gradients)
-    Tg, Eg, E, d, f, k, seed = CASES["fp8_sparse"]
-    inp = make_prerouted_fp8(Tg, Eg, E, d, f, k, seed)
-    counts = np.bincount(inp.topk_ids[inp.topk_ids >= 0], minlength=E)
-    assert (counts == 0).any() and counts.sum() > 0
 
 
 class _DequantExperts:
@@ -106,9 +98,9 @@ def test_fp8_fullsize_dsv3_share():
             "dx": rel_err(to_np(b["dx"])[toks], np.stack([a for a, _ in bw])),
             "d_topk_w": rel_err(to_np(b["d_topk_w"])[toks], np.stack([c for _, c in bw]))}
     # the largest and the smallest expert's weight gradients in full (their whole slices set the
-    # error scale), with the token-axis MX blocks of x and dy the layer uses
+    # error scale)
     for e in (int(np.argmax(pl.counts)), int(np.argmin(pl.counts))):
-        r1, r2 = oracle.expert_weight_grads(x, W1, W2, ids, w, dy, e, q_dw=oracle.mx_roundtrip_rows)
+        r1, r2 = oracle.expert_weight_grads(x, W1, W2, ids, w, dy, e)
         errs[f"dW1[{e}]"] = rel_err(to_np(b["dW1"][e]), r1)
         errs[f"dW2[{e}]"] = rel_err(to_np(b["dW2"][e]), r2)
     # y is linear in the routing weights: sum(dy * y) = sum(w * d_topk_w)

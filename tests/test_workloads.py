@@ -56,3 +56,12 @@ def test_skew_bias_is_zipf_like():
     inp = make_inputs(2048, 128, 128, c["E"], c["k"], seed=3, skew=3.0)
     rank = inp.meta["expert_rank"]
     assert sorted(rank.tolist()) == list(range(1, c["E"] + 1))
+
+
+def test_fp8_sparse_case_has_empty_experts():
+    # the sparse pre-routed fp8 parity case (64 global experts, 6 local, 24 tokens, top-2,
+    # seed 31) exercises experts that receive no token, whose weight gradients must be zero
+    from workloads import make_prerouted_fp8
+    inp = make_prerouted_fp8(24, 64, 6, 256, 256, 2, 31)
+    counts = np.bincount(inp.topk_ids[inp.topk_ids >= 0], minlength=6)
+    assert (counts == 0).any() and counts.sum() > 0
