@@ -17,8 +17,9 @@ MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = 0, 1, 2
 MOE_WS_ROUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD = 0, 1, 2
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
 
-ENTRY_POINTS = ("moe_workspace_bytes", "moe_saved_bytes", "moe_route", "moe_plan", "moe_forward", "moe_backward",
-                "moe_permute", "moe_combine", "moe_mxfp8_quantize", "moe_set_stage_hook", "moe_status_string")
+ENTRY_POINTS = ("moe_workspace_bytes", "moe_saved_bytes", "moe_route", "moe_route_noalloc", "moe_plan",
+                "moe_forward", "moe_backward", "moe_permute", "moe_combine", "moe_mxfp8_quantize",
+                "moe_set_stage_hook", "moe_status_string")
 
 
 class MoeDims(ctypes.Structure):
@@ -56,6 +57,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_workspace_bytes.argtypes = [dp, i32, ctypes.POINTER(sz)]
     lib.moe_saved_bytes.argtypes = [dp, ctypes.POINTER(sz)]
     lib.moe_route.argtypes = [dp] + [vp] * 8 + [sz, vp]
+    lib.moe_route_noalloc.argtypes = [dp] + [vp] * 7 + [vp]
     lib.moe_plan.argtypes = [dp] + [vp] * 6 + [sz, vp]
     lib.moe_forward.argtypes = [dp] + [vp] * 13 + [sz, vp]
     lib.moe_backward.argtypes = [dp] + [vp] * 19 + [sz, vp]
@@ -119,6 +121,12 @@ def moe_route(dm, logits, topk_ids, topk_w, counts, offsets, perm, inv_perm, ws,
     _check("moe_route", load_library().moe_route(
         ctypes.byref(dm), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm),
         _ptr(inv_perm), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_route_noalloc(dm, logits, topk_ids, topk_w, counts, offsets, perm, inv_perm, stream=None):
+    _check("moe_route_noalloc", load_library().moe_route_noalloc(
+        ctypes.byref(dm), _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm),
+        _ptr(inv_perm), _stream(stream)))
 
 
 def moe_plan(dm, topk_ids, counts, offsets, perm, inv_perm, ws, ws_bytes=None, stream=None):
@@ -212,7 +220,7 @@ def alloc_layer_buffers(dm: MoeDims, device="cuda", backward: bool = True) -> di
 
 
 __all__ = ["MoeDims", "MoEError", "dims", "load_library", "status_string", "moe_workspace_bytes", "moe_saved_bytes",
-           "moe_route", "moe_plan", "moe_forward", "moe_backward", "moe_permute", "moe_combine",
+           "moe_route", "moe_route_noalloc", "moe_plan", "moe_forward", "moe_backward", "moe_permute", "moe_combine",
            "moe_mxfp8_quantize", "moe_set_stage_hook", "alloc_layer_buffers", "ENTRY_POINTS", "MOE_BF16",
            "MOE_FP8_E4M3", "MOE_MXFP8", "MOE_WS_ROUTE", "MOE_WS_FORWARD",
            "MOE_WS_BACKWARD", "MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_WORKSPACE",

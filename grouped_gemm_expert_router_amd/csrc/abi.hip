@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -227,6 +229,48 @@ void* g_hook_user = nullptr;
 
 }  // namespace
 
+// Fixed scratch of moe_route_noalloc: the plan's per-(expert, segment) count and base tables,
+// 2*E*S int32 with at most 512 segments and 1024 experts (4 MiB) for every shape check_dims
+// accepts.  Each GPU the library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not the device address: kernels get the address that
+// hipGetSymbolAddress returns for the device (noalloc_scratch below), never the array's name.
+constexpr size_t kRouteScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the device that owns `st`, looked up once per device with that
+// device current (the caller's current device is restored).
+hipError_t noalloc_scratch(hipStream_t st, void** out) {
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = 0;
+    hipError_t r = hipGetDevice(&cur);
+    if (r == hipSuccess && cur != dev) r = hipSetDevice(dev);
+    void* p = nullptr;
+    if (r == hipSuccess) r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (r == hipSuccess) r = back;
+    }
+    g_scratch_err[dev] = r;
+    g_scratch_ptr[dev] = (r == hipSuccess) ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 int moe_workspace_bytes(const moe_dims* dims, int which, size_t* out) {
@@ -281,6 +325,24 @@ int moe_route(const moe_dims* dims, const float* logits, int32_t* topk_ids, floa
   MOE_TRY("router", launch_router(logits, (int)dims->T, (int)dims->E, (int)dims->k, topk_ids, topk_w, st));
   MOE_TRY("plan", launch_plan(topk_ids, A, (int)dims->E, counts, offsets, perm, inv_perm, ws, st));
 
+  return MOE_OK;
+}
+
+int moe_route_noalloc(const moe_dims* dims, const float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                      int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  const int64_t A = dims->T * dims->k;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (A > 0 && (!logits || !topk_ids || !topk_w || !perm || !inv_perm)) return MOE_ERR_NULL;
+  if (plan_ws_bytes(A, dims->E) > kRouteScratchBytes) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  rc = hip_status(noalloc_scratch(st, &ws));
+  if (rc) return rc;
+  // the plan writes every table entry it reads, so the scratch needs no clearing between calls
+  MOE_TRY("router", launch_router(logits, (int)dims->T, (int)dims->E, (int)dims->k, topk_ids, topk_w, st));
+  MOE_TRY("plan", launch_plan(topk_ids, A, (int)dims->E, counts, offsets, perm, inv_perm, ws, st));
   return MOE_OK;
 }
 

@@ -32,7 +32,8 @@
  * Conventions for every call:
  *   - Ownership: the caller allocates every buffer (including `ws` workspace and the `saved`
  *     forward->backward context).  The library allocates nothing and keeps no state between
- *     calls; calls are re-entrant.
+ *     calls; calls are re-entrant.  The one exception is moe_route_noalloc, which takes no
+ *     workspace and uses a fixed device array of the library instead (see there).
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work
  *     on it and return; nothing synchronises the host and no count leaves the device.
  *   - Validation: arguments are checked on the host only.  Device contents are preconditions:
@@ -104,6 +105,17 @@ int moe_saved_bytes(const moe_dims* dims, size_t* out);
 int moe_route(const moe_dims* dims, const float* logits, int32_t* topk_ids, float* topk_w,
               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
               void* ws, size_t ws_bytes, void* stream);
+
+/* moe_route without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same outputs,
+ * bit for bit.  The plan's tables live in a fixed 4 MiB device array inside the library, one per
+ * GPU, held until the process ends; every shape this header accepts fits it (MOE_ERR_WORKSPACE
+ * otherwise).  The call allocates nothing.  All calls on one GPU share that array, so calls that
+ * overlap in time on one GPU (different streams, or different host threads) race and must be
+ * serialised by the caller; calls on one stream are ordered and safe.  The first call on a GPU
+ * looks up the array's device address (MOE_ERR_HIP if that fails). */
+int moe_route_noalloc(const moe_dims* dims, const float* logits, int32_t* topk_ids, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* stream);
 
 /* Expert plan for already-routed pairs: per-expert counts, their exclusive prefix sum and the
  * stable counting sort of pairs by expert (ragged per-expert groups: [JAX] "Az egyenetlen

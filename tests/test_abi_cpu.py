@@ -183,3 +183,14 @@ def test_mxfp8_padded_rows_rule(lib):
     assert sz(lib, moe.dims(T, 256, 256, E, k, dtype=mx), moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
     assert sz(lib, moe.dims(T // 2, 256, 256, E, k, dtype=mx), moe.MOE_WS_FORWARD)[0] == moe.MOE_OK
 
+
+def test_route_noalloc_host_rules(lib):
+    # the fixed 4 MiB scratch holds the plan tables of every shape the ABI accepts: the largest
+    # (1024 experts, T*k just under 2^31) needs exactly 2 * 1024 * 512 int32
+    rc, need = sz(lib, moe.dims(268435455, 128, 128, 1024, 8), moe.MOE_WS_ROUTE)
+    assert rc == 0 and need <= 4 << 20
+    dm = moe.dims(64, 128, 256, 8, 2)
+    outs = [FAKE] * 6       # topk_ids, topk_w, counts, offsets, perm, inv_perm
+    assert lib.moe_route_noalloc(ctypes.byref(dm), None, *outs, None) == moe.MOE_ERR_NULL
+    assert lib.moe_route_noalloc(ctypes.byref(dm), FAKE, *outs[:-1], None, None) == moe.MOE_ERR_NULL
+    assert lib.moe_route_noalloc(ctypes.byref(moe.dims(64, 128, 256, 8, 9)), FAKE, *outs, None) == moe.MOE_ERR_SHAPE
