@@ -528,6 +528,36 @@ def main():
                    "frac_hbm_peak": pby / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del xp
 
+    # router front end (the gate in front of the layer; its logits are the step's input, so it is
+    # timed here on its own): logits = x Wg, then the backward through it (dWg and dx += dl Wg^T)
+    router = None
+    if not fp8 and inp.Wg is not None:
+        Wg = bf16(inp.Wg)
+        lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+        dWg = torch.empty((d, E), dtype=torch.bfloat16, device=dev)
+        rws = torch.empty((max(moe.moe_workspace_bytes(dm, moe.MOE_WS_ROUTER), 256),), dtype=torch.uint8,
+                          device=dev)
+        dxr = b["dx"].clone()
+        moe.moe_router_logits(dm, x, Wg, lg)
+        moe.moe_router_backward(dm, x, Wg, b["d_logits"], dxr, dWg, rws)
+        r0, r1, r2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        reps = 10
+        r0.record(cur)
+        for _ in range(reps):
+            moe.moe_router_logits(dm, x, Wg, lg)
+        r1.record(cur)
+        for _ in range(reps):
+            moe.moe_router_backward(dm, x, Wg, b["d_logits"], dxr, dWg, rws)
+        r2.record(cur)
+        torch.cuda.synchronize()
+        lms, bms = r0.elapsed_time(r1) / reps, r1.elapsed_time(r2) / reps
+        fl = 2.0 * T * d * E
+        router = {"logits_ms": lms, "backward_ms": bms, "logits_tflops": fl / (lms * 1e-3) / 1e12,
+                  "backward_tflops": 2 * fl / (bms * 1e-3) / 1e12,
+                  "note": "x.Wg and its backward (dWg, dx += d_logits.Wg^T), bf16 MFMA; outside the timed step"}
+        log(f"[bench] router front end: logits {lms:.3f} ms, backward {bms:.3f} ms")
+        del lg, dWg, rws, dxr
+
     # LLC-cold steps: a 512 MiB scratch write before each one (outside its timing) evicts the
     # step's operands from the 256 MB last-level cache and the L2s; the median step is reported
     cold = None
@@ -565,7 +595,7 @@ def main():
         "frac_of_bf16_peak": tflops / PEAK_TFLOPS["bf16"],
         "frac_of_mfma_peak": ideal_ms / ms,
         "useful_flop_per_step": useful, "ms_per_step_with_stage_events": ms_ev, "stages": stages,
-        "permute_standalone": permute, "roofline": roof,
+        "permute_standalone": permute, "router_front_end": router, "roofline": roof,
         "llc_cold": cold, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -14,12 +14,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_BF16, MOE_FP8_E4M3, MOE_MXFP8 = 0, 1, 2
-MOE_WS_ROUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD = 0, 1, 2
+MOE_WS_ROUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD, MOE_WS_ROUTER = 0, 1, 2, 3
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
 
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_saved_bytes", "moe_route", "moe_route_noalloc", "moe_plan",
-                "moe_forward", "moe_backward", "moe_permute", "moe_combine", "moe_mxfp8_quantize",
-                "moe_set_stage_hook", "moe_status_string")
+                "moe_forward", "moe_backward", "moe_router_logits", "moe_router_backward", "moe_permute",
+                "moe_combine", "moe_mxfp8_quantize", "moe_set_stage_hook", "moe_status_string")
 
 
 class MoeDims(ctypes.Structure):
@@ -61,6 +61,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_plan.argtypes = [dp] + [vp] * 6 + [sz, vp]
     lib.moe_forward.argtypes = [dp] + [vp] * 13 + [sz, vp]
     lib.moe_backward.argtypes = [dp] + [vp] * 19 + [sz, vp]
+    lib.moe_router_logits.argtypes = [dp, vp, vp, vp, vp]
+    lib.moe_router_backward.argtypes = [dp] + [vp] * 6 + [sz, vp]
     lib.moe_permute.argtypes = [dp, vp, vp, vp, vp]
     lib.moe_combine.argtypes = [dp, vp, vp, vp, vp]
     lib.moe_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, i32, vp, vp, vp]
@@ -153,6 +155,17 @@ def moe_backward(dm, dy, x, x_scale, W1, W1_scale, W2, W2_scale, topk_ids, topk_
         _ptr(dW2), _ptr(d_topk_w), _ptr(d_logits), _ptr(ws), nb, _stream(stream)))
 
 
+def moe_router_logits(dm, x, Wg, logits, stream=None):
+    _check("moe_router_logits", load_library().moe_router_logits(ctypes.byref(dm), _ptr(x), _ptr(Wg), _ptr(logits),
+                                                                 _stream(stream)))
+
+
+def moe_router_backward(dm, x, Wg, d_logits, dx, dWg, ws, ws_bytes=None, stream=None):
+    nb = (ws.numel() * ws.element_size() if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check("moe_router_backward", load_library().moe_router_backward(
+        ctypes.byref(dm), _ptr(x), _ptr(Wg), _ptr(d_logits), _ptr(dx), _ptr(dWg), _ptr(ws), nb, _stream(stream)))
+
+
 def moe_permute(dm, x, inv_perm, xp, stream=None):
     _check("moe_permute", load_library().moe_permute(ctypes.byref(dm), _ptr(x), _ptr(inv_perm), _ptr(xp),
                                                      _stream(stream)))
@@ -220,8 +233,9 @@ def alloc_layer_buffers(dm: MoeDims, device="cuda", backward: bool = True) -> di
 
 
 __all__ = ["MoeDims", "MoEError", "dims", "load_library", "status_string", "moe_workspace_bytes", "moe_saved_bytes",
-           "moe_route", "moe_route_noalloc", "moe_plan", "moe_forward", "moe_backward", "moe_permute", "moe_combine",
+           "moe_route", "moe_route_noalloc", "moe_plan", "moe_forward", "moe_backward", "moe_router_logits",
+           "moe_router_backward", "moe_permute", "moe_combine",
            "moe_mxfp8_quantize", "moe_set_stage_hook", "alloc_layer_buffers", "ENTRY_POINTS", "MOE_BF16",
            "MOE_FP8_E4M3", "MOE_MXFP8", "MOE_WS_ROUTE", "MOE_WS_FORWARD",
-           "MOE_WS_BACKWARD", "MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_WORKSPACE",
+           "MOE_WS_BACKWARD", "MOE_WS_ROUTER", "MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_ERR_ALIGN"]

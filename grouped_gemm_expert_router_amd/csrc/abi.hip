@@ -281,6 +281,7 @@ int moe_workspace_bytes(const moe_dims* dims, int which, size_t* out) {
     case MOE_WS_ROUTE: *out = al256(plan_ws_bytes(dims->T * dims->k, dims->E)); return MOE_OK;
     case MOE_WS_FORWARD: *out = fwd_layout(dims).total; return MOE_OK;
     case MOE_WS_BACKWARD: *out = bwd_layout(dims).total; return MOE_OK;
+    case MOE_WS_ROUTER: *out = al256(router_ws_bytes(dims->T, (int)dims->d, (int)dims->E)); return MOE_OK;
     default: return MOE_ERR_SHAPE;
   }
 }
@@ -536,6 +537,40 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   MOE_TRY("dlogits", launch_dlogits(dwp, dact_parts(dims), inv_perm, topk_ids, topk_w, s.T, s.E, s.k, d_topk_w, d_logits,
                                    st));
 
+  return MOE_OK;
+}
+
+int moe_router_logits(const moe_dims* dims, const void* x, const void* Wg, float* logits, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->dtype == MOE_FP8_E4M3) return MOE_ERR_DTYPE;  // the gate reads x in bf16
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !Wg || !logits) return MOE_ERR_NULL;
+  if (!al16(x) || !al16(Wg) || !al16(logits)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("router_logits", launch_router_logits((const uint16_t*)x, (const uint16_t*)Wg, (int)dims->T,
+                                                (int)dims->d, (int)dims->E, logits, st));
+  return MOE_OK;
+}
+
+int moe_router_backward(const moe_dims* dims, const void* x, const void* Wg, const float* d_logits, void* dx,
+                        void* dWg, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->dtype == MOE_FP8_E4M3) return MOE_ERR_DTYPE;
+  const int T = (int)dims->T, d = (int)dims->d, E = (int)dims->E;
+  const size_t need = al256(router_ws_bytes(dims->T, d, E));
+  if (dWg && need > 0 && !ws) return MOE_ERR_NULL;
+  if (dWg && ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (T > 0 && (dx || dWg) && (!d_logits || (dWg && !x) || (dx && !Wg))) return MOE_ERR_NULL;
+  if ((x && !al16(x)) || (Wg && !al16(Wg)) || (d_logits && !al16(d_logits)) || (dx && !al16(dx)) ||
+      (dWg && !al16(dWg)) || (ws && !al256p(ws)))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  if (dx && T > 0)
+    MOE_TRY("router_dx", launch_router_dx(d_logits, (const uint16_t*)Wg, T, d, E, (uint16_t*)dx, st));
+  // an empty layer still writes dWg (zeros)
+  if (dWg) MOE_TRY("router_dwg", launch_router_dwg((const uint16_t*)x, d_logits, T, d, E, (uint16_t*)dWg, (float*)ws, st));
   return MOE_OK;
 }
 

@@ -131,6 +131,18 @@ hipError_t launch_mx_dx(const MoeShape& s, const uint8_t* dHq, const uint8_t* dH
                         const uint8_t* W1e, const int32_t* offsets, const int32_t* perm, const int2* tiles,
                         const int32_t* ntiles, uint16_t* dXp, hipStream_t st);
 
+// router front end (dense gate products, bf16 MFMA): logits = x Wg; dx += d_logits Wg^T;
+// dWg = x^T d_logits with the token axis cut into slices whose fp32 partials (router_ws_bytes) are
+// summed in slice order
+void router_dwg_split(int64_t T, int d, int E, int* slices, int* kslice);
+size_t router_ws_bytes(int64_t T, int d, int E);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wg, int T, int d, int E, float* logits,
+                                hipStream_t st);
+hipError_t launch_router_dx(const float* d_logits, const uint16_t* Wg, int T, int d, int E, uint16_t* dx,
+                            hipStream_t st);
+hipError_t launch_router_dwg(const uint16_t* x, const float* d_logits, int T, int d, int E, uint16_t* dWg,
+                             float* partial, hipStream_t st);
+
 // data movement and router backward
 hipError_t launch_permute(const uint16_t* x, const int32_t* inv_perm, int T, int d, int k, uint16_t* xp,
                           hipStream_t st);

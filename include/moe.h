@@ -88,10 +88,11 @@ enum {
   MOE_ERR_ALIGN = -6      /* a device buffer is not 16-byte aligned (ws and saved: 256) */
 };
 
-enum { MOE_WS_ROUTE = 0, MOE_WS_FORWARD = 1, MOE_WS_BACKWARD = 2 };
+enum { MOE_WS_ROUTE = 0, MOE_WS_FORWARD = 1, MOE_WS_BACKWARD = 2, MOE_WS_ROUTER = 3 };
 
 /* Workspace bytes needed by moe_route/moe_plan (which = MOE_WS_ROUTE), moe_forward
- * (MOE_WS_FORWARD) or moe_backward (MOE_WS_BACKWARD).  Host only. */
+ * (MOE_WS_FORWARD), moe_backward (MOE_WS_BACKWARD) or moe_router_backward (MOE_WS_ROUTER).
+ * Host only. */
 int moe_workspace_bytes(const moe_dims* dims, int which, size_t* out);
 
 /* Bytes of the `saved` context moe_forward writes and moe_backward reads (the GEMM1 output
@@ -165,6 +166,25 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
                  const int32_t* perm, const int32_t* inv_perm, const void* saved, void* dx,
                  void* dW1, void* dW2, float* d_topk_w, float* d_logits, void* ws,
                  size_t ws_bytes, void* stream);
+
+/* Router scores (the gate in front of moe_route): logits[T, E] = x[T, d] . Wg[d, E] with bf16 x and
+ * gate weight Wg (row-major [d, E]), fp32 accumulation and fp32 output ([JAX] "A dropless MoE
+ * minden tokent feldolgoz": a learned router scores the experts and keeps the top K).  Feeding
+ * these logits to moe_route gives the layer's routing.  dtype MOE_BF16 or MOE_MXFP8 (x is bf16 in
+ * both; MOE_FP8_E4M3: MOE_ERR_DTYPE).  x, Wg and logits 16-byte aligned; T = 0 does nothing. */
+int moe_router_logits(const moe_dims* dims, const void* x, const void* Wg, float* logits, void* stream);
+
+/* Backward through moe_router_logits for the layer's d_logits [T, E] (fp32, as moe_backward writes
+ * it).  dWg = x^T . d_logits (bf16 [d, E], fp32 accumulation) when dWg is not NULL: the token axis
+ * is cut into slices whose fp32 partial sums live in `ws` (moe_workspace_bytes(MOE_WS_ROUTER)) and
+ * are added in slice order, so the result is bitwise reproducible; an empty layer (T = 0) writes
+ * zeros.  When dx is not NULL, the part of the input gradient that flows through the logits is
+ * added to it in place: dx[t] = bf16(dx[t] + sum_e d_logits[t, e] Wg[:, e]), the sum in fp32 and
+ * one rounding (pass moe_backward's dx to get the whole input gradient of the routed layer).
+ * d_logits enters the MFMA rounded to bf16.  Same dtype, alignment and workspace rules as the
+ * other calls (ws 256-byte aligned). */
+int moe_router_backward(const moe_dims* dims, const void* x, const void* Wg, const float* d_logits,
+                        void* dx, void* dWg, void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatch on its own (bf16): for every slot with pos = inv_perm[t*k+j] >= 0, xp[pos] = x[t]
  * (so xp[pos] = x[perm[pos] / k] for pos < offsets[E]); rows of xp at or past offsets[E] are left

@@ -30,6 +30,9 @@ What is computed, and where the pages state it:
   backward the gradient of that forward pass ([Prime] "Mit csinált a Prime Intellect?" [what
            did Prime Intellect do?]: a backward for the fused MoE kernel): dx, dW1, dW2,
            d(routing weights) and d(logits) through the top-k softmax.
+  router   the learned router's scores, logits = x Wg with the gate weight Wg [d, E] ([JAX] "A
+           dropless MoE minden tokent feldolgoz"), and their gradients dWg and the part of dx
+           that flows through the logits.
 
 Conventions: W1[e] is [d, 2f] with gate columns [0, f) and up columns [f, 2f);
 SwiGLU(g, u) = silu(g) * u with silu(g) = g * sigmoid(g).  A pair p = t*k + j is slot j of
@@ -305,3 +308,20 @@ def d_logits_from_dw(w, dw, ids, E):
     dl = np.zeros((T, E))
     dl[np.arange(T)[:, None], ids] = w * (dw - inner)
     return dl
+
+
+# --------------------------------------------------------------------------- router front end
+def router_logits(x, Wg):
+    """Router scores logits[t, e] = sum_i x[t, i] Wg[i, e] for the gate weight Wg [d, E]."""
+    return np.asarray(x, np.float64) @ np.asarray(Wg, np.float64)
+
+
+def router_backward(x, Wg, d_logits):
+    """Gradients through logits = x Wg for an upstream d_logits [T, E]: returns
+    (dx_router [T, d], dWg [d, E]) with dx_router[t, i] = sum_e d_logits[t, e] Wg[i, e] (the part of
+    dx that flows through the router, to be added to the expert path's dx) and
+    dWg[i, e] = sum_t x[t, i] d_logits[t, e]."""
+    x = np.asarray(x, np.float64)
+    Wg = np.asarray(Wg, np.float64)
+    dl = np.asarray(d_logits, np.float64)
+    return dl @ Wg.T, x.T @ dl

@@ -65,7 +65,7 @@ def test_dtype_and_reserved_errors(lib):
     assert sz(lib, dm, moe.MOE_WS_FORWARD)[0] == moe.MOE_ERR_SHAPE
     assert lib.moe_workspace_bytes(None, 0, None) == moe.MOE_ERR_NULL
     assert lib.moe_workspace_bytes(ctypes.byref(moe.dims(64, 128, 256, 8, 2)), 0, None) == moe.MOE_ERR_NULL
-    assert sz(lib, moe.dims(64, 128, 256, 8, 2), 3)[0] == moe.MOE_ERR_SHAPE
+    assert sz(lib, moe.dims(64, 128, 256, 8, 2), 4)[0] == moe.MOE_ERR_SHAPE
 
 
 def test_fp8_shape_rules(lib):
@@ -194,3 +194,24 @@ def test_route_noalloc_host_rules(lib):
     assert lib.moe_route_noalloc(ctypes.byref(dm), None, *outs, None) == moe.MOE_ERR_NULL
     assert lib.moe_route_noalloc(ctypes.byref(dm), FAKE, *outs[:-1], None, None) == moe.MOE_ERR_NULL
     assert lib.moe_route_noalloc(ctypes.byref(moe.dims(64, 128, 256, 8, 9)), FAKE, *outs, None) == moe.MOE_ERR_SHAPE
+
+
+def test_router_front_end_host_rules(lib):
+    F = FAKE
+    dm = moe.dims(4096, 256, 128, 64, 4)
+    rc, need = sz(lib, dm, moe.MOE_WS_ROUTER)
+    # dWg's token slices: fp32 partials of the whole [d, E] gradient per slice
+    assert rc == 0 and need % 256 == 0 and need >= 2 * 256 * 64 * 4
+    lg = lambda *a, d=dm: lib.moe_router_logits(ctypes.byref(d), *a, None)
+    assert lg(None, F, F) == moe.MOE_ERR_NULL
+    assert lg(F, F, F + 4) == moe.MOE_ERR_ALIGN
+    assert lg(F, F, F, d=moe.dims(64, 256, 256, 8, 2, dtype=moe.MOE_FP8_E4M3)) == moe.MOE_ERR_DTYPE
+    assert lg(None, None, None, d=moe.dims(0, 128, 128, 8, 2)) == moe.MOE_OK
+    bw = lambda x, wg, dl, dx, dwg, ws, nb: lib.moe_router_backward(ctypes.byref(dm), x, wg, dl, dx, dwg, ws, nb, None)
+    assert bw(F, F, None, F, F, F, need, ) == moe.MOE_ERR_NULL          # d_logits
+    assert bw(None, F, F, None, F, F, need) == moe.MOE_ERR_NULL         # dWg needs x
+    assert bw(F, None, F, F, None, F, need) == moe.MOE_ERR_NULL         # dx needs Wg
+    assert bw(F, F, F, None, F, None, need) == moe.MOE_ERR_NULL         # dWg needs the workspace
+    assert bw(F, F, F, None, F, F, need - 256) == moe.MOE_ERR_WORKSPACE
+    assert bw(F, F, F, None, F, F + 16, need) == moe.MOE_ERR_ALIGN
+    assert bw(None, None, None, None, None, None, 0) == moe.MOE_OK     # nothing requested

@@ -239,6 +239,48 @@ def test_logit_gradient_matches_central_differences():
     _fd_check(fun, L, b["d_logits"], range(L.size))
 
 
+def _routed_layer_loss(x, Wg, W1, W2, dy, k, ids_fixed):
+    """L = sum(dy * y) of the layer routed by its own router: logits = x Wg, top-k, softmax."""
+    ids, w = oracle.route(oracle.router_logits(x, Wg), k)
+    assert np.array_equal(ids, ids_fixed)               # the top-k set stays fixed under h
+    return _loss(x, W1, W2, ids, w, dy)
+
+
+def test_router_gradients_match_central_differences():
+    """Central differences of the whole routed layer (router scores -> top-k softmax -> experts)
+    with respect to the gate weight and the input: dWg = router_backward's dWg; dx = the expert
+    path's dx plus router_backward's dx_router (x reaches the loss through both)."""
+    T, d, f, E, k = 7, 6, 4, 6, 2
+    x, W1, W2, _, dy = rand_layer(T, d, f, E, k, 25)
+    g = np.random.default_rng(3)
+    Wg = g.standard_normal((d, E)) / np.sqrt(d)
+    L = oracle.router_logits(x, Wg)
+    srt = np.sort(L, axis=1)[:, ::-1]
+    assert np.all(srt[:, k - 1] - srt[:, k] > 1e-3)
+    ids, w = oracle.route(L, k)
+    b = oracle.backward(x, W1, W2, ids, w, dy)
+    dx_r, dWg = oracle.router_backward(x, Wg, b["d_logits"])
+    fun = lambda: _routed_layer_loss(x, Wg, W1, W2, dy, k, ids)
+    _fd_check(fun, Wg, dWg, range(Wg.size))
+    _fd_check(fun, x, b["dx"] + dx_r, range(x.size))
+    # and the expert path alone is not the whole input gradient (the router term is not zero)
+    assert np.abs(dx_r).max() > 1e-3 * np.abs(b["dx"]).max()
+
+
+def test_router_logits_against_per_entry_sums_and_linearity():
+    g = np.random.default_rng(4)
+    x, Wg = g.standard_normal((9, 5)), g.standard_normal((5, 7))
+    L = oracle.router_logits(x, Wg)
+    for t, e in [(0, 0), (8, 6), (3, 2), (5, 4)]:
+        assert abs(L[t, e] - math.fsum(x[t, i] * Wg[i, e] for i in range(5))) <= 1e-12
+    dl = g.standard_normal((9, 7))
+    dx_r, dWg = oracle.router_backward(x, Wg, dl)
+    assert dx_r.shape == x.shape and dWg.shape == Wg.shape
+    # logits are bilinear in (x, Wg): <dWg, Wg> = <dx_r, x> = <d_logits, logits>
+    np.testing.assert_allclose(np.sum(dWg * Wg), np.sum(dl * L), rtol=1e-12)
+    np.testing.assert_allclose(np.sum(dx_r * x), np.sum(dl * L), rtol=1e-12)
+
+
 def test_dlogits_rows_sum_to_zero_and_inner_product_identities():
     T, d, f, E, k = 40, 8, 6, 6, 2
     x, W1, W2, L, dy = rand_layer(T, d, f, E, k, 23)

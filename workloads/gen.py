@@ -164,6 +164,8 @@ class MoEInputs:
     W2: np.ndarray                  # [E, f, d]
     dy: Optional[np.ndarray]        # [T, d] bf16 upstream gradient
     logits: Optional[np.ndarray] = None     # [T, E] fp32 router logits (routed configs)
+    Wg: Optional[np.ndarray] = None         # [d, E] bf16 gate weight: the same draw that made the
+                                            # logits, rounded to bf16 (input of the router front end)
     topk_ids: Optional[np.ndarray] = None   # [T, k] int32, -1 = slot owned by another rank
     topk_w: Optional[np.ndarray] = None     # [T, k] fp32 routing weights (pre-routed configs)
     x_scale: Optional[np.ndarray] = None    # fp8: [T, d/128]
@@ -177,6 +179,8 @@ def make_inputs(T: int, d: int, f: int, E: int, k: int, seed: int = 0, *, skew: 
                 identical_experts: bool = False) -> MoEInputs:
     """bf16 layer with router logits = x @ Wg (+ bias).  Distribution recipe:
     x ~ N(0,1); W1 ~ N(0, 1/d); W2 ~ N(0, 1/f); Wg ~ N(0, 1/d) in fp32; dy ~ N(0,1).
+    The fp32 logits are computed here from the fp32 Wg; Wg is also handed out rounded to bf16
+    for the router front end, which computes its own logits from it.
     skew > 0 adds b_e = skew * ln(1/rank_e) for a seeded random ranking 1..E of the experts."""
     x = _normal_bf16((T, d), seed, 1, 1.0)
     if identical_experts:
@@ -199,7 +203,7 @@ def make_inputs(T: int, d: int, f: int, E: int, k: int, seed: int = 0, *, skew: 
         logits = (logits + logits_bias.astype(np.float32)).astype(np.float32)
     dy = _normal_bf16((T, d), seed, 6, 1.0) if with_dy else None
     return MoEInputs(name=name, T=T, d=d, f=f, E=E, k=k, dtype="bf16", x=x, W1=W1, W2=W2, dy=dy,
-                     logits=np.ascontiguousarray(logits), meta=meta)
+                     logits=np.ascontiguousarray(logits), Wg=bf16_bits_from_f32(Wg), meta=meta)
 
 
 def make_prerouted_fp8(T_global: int, E_global: int, E: int, d: int, f: int, k: int, seed: int,
