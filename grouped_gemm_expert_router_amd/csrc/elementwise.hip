@@ -89,9 +89,10 @@ hipError_t launch_combine(const uint16_t* op, const int32_t* inv_perm, int T, in
 }
 
 // Router backward, one wave per token.  d_topk_w[p] = sum over column tiles of the partial
-// inner products <dL/dAs, a> (fixed order); d_logits[t, ids[t,j]] =
+// inner products <dL/dAs, a> (fixed order; partial q of sorted row pos at dwp[q*stride + pos]);
+// d_logits[t, ids[t,j]] =
 // w_j (d_topk_w_j - sum_i w_i d_topk_w_i), zero for experts outside the token's top-k.
-__global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ dwp, int nparts,
+__global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ dwp, int nparts, int64_t stride,
                                                       const int32_t* __restrict__ inv_perm,
                                                       const int32_t* __restrict__ ids,
                                                       const float* __restrict__ topk_w, int T, int E, int k,
@@ -107,11 +108,11 @@ __global__ __launch_bounds__(256) void dlogits_kernel(const float* __restrict__ 
     const int pos = inv_perm[p];
     if (pos >= 0) {
       // partials summed in part order; loaded 4 at a time so the loads overlap
-      const float* src = dwp + (int64_t)pos * nparts;
+      const float* src = dwp + pos;
       for (int q0 = 0; q0 < nparts; q0 += 4) {
         float v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = q0 + u < nparts ? src[q0 + u] : 0.0f;
+        for (int u = 0; u < 4; ++u) v[u] = q0 + u < nparts ? src[(int64_t)(q0 + u) * stride] : 0.0f;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (q0 + u < nparts) dw += v[u];
@@ -139,7 +140,9 @@ hipError_t launch_dlogits(const float* dwp, int nparts, const int32_t* inv_perm,
                           const float* topk_w, int T, int E, int k, float* d_topk_w, float* d_logits, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const size_t lds = d_logits ? 4 * (size_t)E * sizeof(float) : 0;
-  dlogits_kernel<<<(T + 3) / 4, 256, lds, st>>>(dwp, nparts, inv_perm, ids, topk_w, T, E, k, d_topk_w, d_logits);
+  const int64_t stride = (int64_t)T * k;  // partials are part-major over the T*k sorted positions
+  dlogits_kernel<<<(T + 3) / 4, 256, lds, st>>>(dwp, nparts, stride, inv_perm, ids, topk_w, T, E, k, d_topk_w,
+                                                 d_logits);
   return hipGetLastError();
 }
 

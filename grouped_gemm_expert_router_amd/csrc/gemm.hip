@@ -53,8 +53,8 @@ struct GemmArgs {
   int64_t ldc1;
   const uint16_t* Hs;
   int64_t ldh;
-  float* dwp;
-  int nparts;
+  float* dwp;        // d_topk_w partials, part-major: partial q of sorted row pos at dwp[q*dwp_stride + pos]
+  int64_t dwp_stride;
   // ragged K split: work unit u = (expert, chunk) of KC rows; experts split into several chunks
   // write fp32 partials (slot wg_pslot[e] + chunk) that a second kernel sums in chunk order
   const int2* wg_units;
@@ -105,6 +105,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
   __shared__ float s_w[RAGGED_K ? 1 : BM];
   __shared__ int s_slot[RAGGED_K ? 1 : BM];
+  __shared__ float s_part[MODE == M_DACT ? WN : 1][MODE == M_DACT ? BM : 1];  // DACT: per-wave-column partials
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -463,8 +464,9 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   } else if constexpr (MODE == M_DACT) {
     static_assert(WN == 4, "the d_topk_w part count assumes 4 waves across N");
     // G = dL/dAs.  a = silu(g) u from the saved H; da = w G; dH = [da u sig(g) (1 + g (1 - sig(g))),
-    // da silu(g)]; the d_topk_w partial <G, a> of a row over this wave's columns goes to part
-    // nt * WN + wn.  The H of block (i+1, j) is loaded as soon as block (i, j) is done with its
+    // da silu(g)]; the d_topk_w partial <G, a> of a row over the tile's columns is summed over the
+    // WN wave columns in LDS (in wave-column order) and stored once per row as part nt, rows
+    // consecutive.  The H of block (i+1, j) is loaded as soon as block (i, j) is done with its
     // registers, so the loads overlap the remaining blocks' arithmetic.
     uint4 hg[FN][2], hu[FN][2];
     auto load_h = [&](int i, int j) __attribute__((always_inline)) {
@@ -533,7 +535,14 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
         if (i + 1 < FM) load_h(i + 1, j);
       }
       part += __shfl_xor(part, 32, 64);  // lanes l and l+32 hold the same row
-      if (ok && h == 0) g.dwp[pos * g.nparts + nt * WN + wn] = part;
+      if (h == 0) s_part[wn][lr] = part;
+    }
+    __syncthreads();
+    for (int r = tid; r < BM; r += NTH) {
+      float sum = s_part[0][r];
+#pragma unroll
+      for (int c = 1; c < WN; ++c) sum += s_part[c][r];
+      if (r < mrows) g.dwp[(int64_t)nt * g.dwp_stride + m0 + r] = sum;
     }
   } else if (RAGGED_K && pslot >= 0) {
     // one chunk of a split expert: fp32 partial, summed later in chunk order; each 4-column
@@ -621,9 +630,8 @@ GemmArgs base_args(const MoeShape& s, const int32_t* offsets, const int32_t* per
 }  // namespace
 
 int dact_bn(int f) { return pick_bn(f); }
-// d_topk_w partials per pair: one per (N tile, wave column); the 256 x BN tiles of the
-// activation-gradient GEMM run 4 waves across N
-int dact_parts_bf16(int f) { return (f / dact_bn(f)) * 4; }
+// d_topk_w partials per pair: one per N tile of the activation-gradient GEMM
+int dact_parts_bf16(int f) { return f / dact_bn(f); }
 
 int max_row_tiles(int64_t A, int E, int bm) {
   const int64_t t = (A + bm - 1) / bm + (A < E ? A : E);
@@ -690,8 +698,8 @@ hipError_t launch_gemm_dact(const MoeShape& s, const uint16_t* dy, const uint16_
   g.C0 = dH;
   g.ldc0 = 2 * (int64_t)s.f;
   g.dwp = dwp;
+  g.dwp_stride = (int64_t)s.T * s.k;
   const int bn = dact_bn(s.f);
-  g.nparts = dact_parts_bf16(s.f);
   const int64_t A = (int64_t)s.T * s.k;
   dim3 grid((unsigned)(max_row_tiles(A, s.E, kGemmBM) * (s.f / bn)));
   return run<M_DACT>(g, kGemmBM, bn, grid, st);

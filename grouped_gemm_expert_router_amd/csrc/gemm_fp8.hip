@@ -57,8 +57,8 @@ struct Fp8Args {
   int64_t ldqs;
   const uint16_t* Hs;
   int64_t ldh;
-  float* dwp;
-  int nparts;
+  float* dwp;  // d_topk_w partials, part-major: dwp[part * dwp_stride + pos]
+  int64_t dwp_stride;
 };
 
 // Quantise 8 values of a 128-wide block held by 16 consecutive lanes: scale = amax / 448 of the
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
             g.QS[pos * g.ldqs + col / 128] = sg_;
             g.QS[pos * g.ldqs + (g.f + col) / 128] = su_;
           }
-          if (cc == 0) g.dwp[pos * g.nparts + nt] = part;
+          if (cc == 0) g.dwp[nt * g.dwp_stride + pos] = part;
         }
       }
     } else {
@@ -478,7 +478,7 @@ hipError_t launch_fp8_dact(const MoeShape& s, const uint8_t* dyq, const float* d
   g.QS = dHs;
   g.ldqs = 2 * s.f / 128;
   g.dwp = dwp;
-  g.nparts = s.f / 256;
+  g.dwp_stride = (int64_t)s.T * s.k;  // one partial per 256-column N tile
   return run_fp8<F_DACT>(g, (int64_t)s.T * s.k, s.E, s.f / 256, st);
 }
 

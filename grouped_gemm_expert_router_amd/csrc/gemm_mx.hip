@@ -53,8 +53,8 @@ struct MxArgs {
   int64_t ldqe;
   const uint16_t* Hs;
   int64_t ldh;
-  float* dwp;
-  int nparts;
+  float* dwp;  // d_topk_w partials, part-major: dwp[part * dwp_stride + pos]
+  int64_t dwp_stride;
 };
 
 // Shared exponent s of a block with maximum magnitude amax: the smallest s with
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
             g.Qe[pos * g.ldqe + col / 32] = (uint8_t)eg;
             g.Qe[pos * g.ldqe + (g.f + col) / 32] = (uint8_t)eu;
           }
-          if (cc == 0) g.dwp[pos * g.nparts + nt] = part;
+          if (cc == 0) g.dwp[nt * g.dwp_stride + pos] = part;
         }
       }
     } else {
@@ -630,7 +630,7 @@ hipError_t launch_mx_dact(const MoeShape& s, const uint8_t* dyq, const uint8_t* 
   g.Qe = dHe;
   g.ldqe = 2 * s.f / 32;
   g.dwp = dwp;
-  g.nparts = s.f / 256;
+  g.dwp_stride = (int64_t)s.T * s.k;  // one partial per 256-column N tile
   return run_mx<X_DACT>(g, (int64_t)s.T * s.k, s.E, s.f / 256, st);
 }
 
