@@ -3,7 +3,8 @@ Mixtral-8x7B shapes), in the same launch configuration bench.py times.
 
 Routing and the plan are compared bit for bit with the oracle on the full inputs.  Float outputs
 are compared on sampled rows and entries that the oracle computes one by one (per-token forward
-and backward, single weight-gradient entries), plus identities that hold at any size: empty
+and backward, single weight-gradient entries), on whole weight-gradient slices of selected
+experts (computed from those experts' rows only), plus identities that hold at any size: empty
 experts get exactly zero weight gradients, and sum(dy*y) = sum(w*d_topk_w) = sum(W2*dW2)."""
 import numpy as np
 import pytest
@@ -39,7 +40,7 @@ def test_fullsize_parity(name):
     wr = w  # fp64 routing weights of the oracle
 
     b = gl.b
-    toks = _sample_tokens(inp.T, 6 if name == "mixtral" else 14, 1)
+    toks = _sample_tokens(inp.T, 12 if name == "mixtral" else 48, 1)
     y_g, dx_g = to_np(b["y"])[toks], to_np(b["dx"])[toks]
     dtw_g, dl_g = to_np(b["d_topk_w"])[toks], to_np(b["d_logits"])[toks]
     y_o = np.stack([oracle.token_forward(x32[t].astype(np.float64), W1, W2, ids[t], wr[t]) for t in toks])
@@ -55,16 +56,26 @@ def test_fullsize_parity(name):
     g = np.random.default_rng(2)
     experts = np.unique(np.concatenate([[int(np.argmax(pl.counts))], np.flatnonzero(pl.counts)[:: max(1, inp.E // 6)]]))
     for e in experts:
-        ri, cj = g.integers(0, inp.d, 12), g.integers(0, 2 * inp.f, 12)
+        ri, cj = g.integers(0, inp.d, 48), g.integers(0, 2 * inp.f, 48)
         ref = oracle.weight_grad_entries(x32, W1, W2, ids, wr, dy32, e, ri, cj, "dW1")
         got = dW1_g[e][torch.from_numpy(ri).cuda(), torch.from_numpy(cj).cuda()].float().cpu().numpy()
         errs[f"dW1[{e}]"] = rel_err(got, ref)
-        ri, cj = g.integers(0, inp.f, 12), g.integers(0, inp.d, 12)
+        ri, cj = g.integers(0, inp.f, 48), g.integers(0, inp.d, 48)
         ref = oracle.weight_grad_entries(x32, W1, W2, ids, wr, dy32, e, ri, cj, "dW2")
         got = dW2_g[e][torch.from_numpy(ri).cuda(), torch.from_numpy(cj).cuda()].float().cpu().numpy()
         errs[f"dW2[{e}]"] = rel_err(got, ref)
     for e in np.flatnonzero(pl.counts == 0):
         assert not torch.any(dW1_g[e] != 0) and not torch.any(dW2_g[e] != 0), f"empty expert {e}"
+    # whole weight-gradient slices, element by element, of the smallest routed expert and (where
+    # its rows are few enough for the fp64 oracle: the Qwen3 shape) of the largest
+    whole = [int(np.flatnonzero(pl.counts)[np.argmin(pl.counts[pl.counts > 0])])]
+    if name == "qwen3":
+        whole.append(int(np.argmax(pl.counts)))
+    if name != "mixtral":
+        for e in whole:
+            r1, r2 = oracle.expert_weight_grads(x32, W1, W2, ids, wr, dy32, e)
+            errs[f"dW1[{e}] whole"] = rel_err(to_np(dW1_g[e]), r1)
+            errs[f"dW2[{e}] whole"] = rel_err(to_np(dW2_g[e]), r2)
 
     # sum(dy*y) = sum(w*dw) = sum(W2*dW2): y is linear in the routing weights and in W2
     lhs = float((gl.dy.double() * b["y"].double()).sum())
