@@ -210,16 +210,18 @@ def make_prerouted_fp8(T_global: int, E_global: int, E: int, d: int, f: int, k: 
                        name: str = "dsv3_fp8") -> MoEInputs:
     """One rank's share of an expert-parallel layer, already routed, in blockwise fp8.
 
-    Each of T_global tokens picks k distinct experts of E_global uniformly at random (the
-    top-k set of i.i.d. continuous logits is a uniform k-subset) with weights drawn from a
-    flat Dirichlet and ordered descending, so each token's k weights sum to 1.  This rank owns
-    experts [0, E); it receives every token with at least one local slot once, and non-local
-    slots carry expert id -1.  Activations and weights are drawn in fp32 and quantised to
-    e4m3 (x per 1x128 block along d, W per 128x128 block); dy is bf16."""
+    Each of T_global tokens draws i.i.d. N(0,1) router logits over the E_global experts and
+    keeps the k largest (descending; a tie has probability zero), with routing weights the
+    softmax over those k logits, so each token's k weights sum to 1.  This rank owns experts
+    [0, E); it receives every token with at least one local slot once, and non-local slots
+    carry expert id -1.  Activations and weights are drawn in fp32 and quantised to e4m3 (x per
+    1x128 block along d, W per 128x128 block); dy is bf16."""
     g = np.random.default_rng((seed, 10))
-    choice = g.permuted(np.tile(np.arange(E_global, dtype=np.int32), (T_global, 1)), axis=1)[:, :k]
-    wts = g.dirichlet(np.ones(k), size=T_global).astype(np.float32)
-    wts = -np.sort(-wts, axis=1)
+    logits = g.standard_normal((T_global, E_global), dtype=np.float32)
+    choice = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
+    top = np.take_along_axis(logits, choice, axis=1).astype(np.float64)
+    z = np.exp(top - top[:, :1])
+    wts = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
     local = choice < E
     recv = np.flatnonzero(local.any(axis=1))
     ids = np.where(local[recv], choice[recv], -1).astype(np.int32)
