@@ -367,6 +367,32 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // dA epilogue staging.  Row block i (32 rows) of wave (wm, wn) keeps its saved H, and then
+  // its dH in place, in a slot of LDS: stage i % 2, offset EP_SLOT * wave.  The slot holds the
+  // wave's TN gate columns of the 32 rows (KM layout of a TN-deep tile: rows of EP_RB bytes,
+  // 16-byte chunks XOR-swizzled), then their TN up columns.  A DMA or store instruction moves
+  // EP_RPI whole rows of one half; a row of the wave's 64 gate (or up) columns is one whole
+  // 128-byte line of H or dH (TN = 64), or half of one (TN = 32).
+  constexpr int EP_RB = TN * 2, EP_HALF = 32 * EP_RB, EP_SLOT = 2 * EP_HALF;
+  constexpr int EP_CPR = TN / 8, EP_RPI = 64 / EP_CPR, EP_QH = 32 / EP_RPI, EP_Q = 2 * EP_QH;
+  static_assert(MODE != M_DACT || ((TN == 64 || TN == 32) && TM == 128 && NW * EP_SLOT <= STAGE),
+                "dA epilogue slots");
+  // H rows of row block i into stage st; a row past the expert's end reads row m0
+  auto dact_h_dma = [&](int i, int st) __attribute__((always_inline)) {
+    if constexpr (MODE == M_DACT) {
+      const uint32_t slot = lds0 + st * STAGE + wave * EP_SLOT;
+      const int rl = lane / EP_CPR, pc = lane % EP_CPR;
+#pragma unroll
+      for (int q = 0; q < EP_Q; ++q) {
+        const int half = q / EP_QH, r = EP_RPI * (q % EP_QH) + rl;
+        const int lr = wm * TM + 32 * i + r;
+        const int64_t pos = m0 + (lr < mrows ? lr : 0);
+        const int c = pc ^ km_swz<TN>(r);  // the logical chunk that physical chunk pc holds
+        dma16(g.Hs + pos * g.ldh + half * g.f + n0 + wn * TN + 8 * c, slot + half * EP_HALF + (q % EP_QH) * 1024);
+      }
+    }
+  };
+
   // ------------------------------------------------------------------ main loop
   // Stage t%S holds tile t.  Iteration t: wait until tile t's DMA has landed (tiles t+1..t+S-2
   // may stay in flight) and all waves are past tile t-1, refill tile t-1's stage with tile
@@ -399,6 +425,10 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
       }
     }
     if (refill) issue(it + S - 1, (it + S - 1) % S, tk);
+    // dA: the H lines of the epilogue's first row block land in the stage the last k step
+    // does not read, under that step's MFMAs
+    if constexpr (MODE == M_DACT)
+      if (it == nk - 1 && busy) dact_h_dma(0, (it + 1) % S);
     if (busy) compute(it % S);
   }
 
@@ -466,27 +496,26 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     // G = dL/dAs.  a = silu(g) u from the saved H; da = w G; dH = [da u sig(g) (1 + g (1 - sig(g))),
     // da silu(g)]; the d_topk_w partial <G, a> of a row over the tile's columns is summed over the
     // WN wave columns in LDS (in wave-column order) and stored once per row as part nt, rows
-    // consecutive.  The H of block (i+1, j) is loaded as soon as block (i, j) is done with its
-    // registers, so the loads overlap the remaining blocks' arithmetic.
-    uint4 hg[FN][2], hu[FN][2];
-    auto load_h = [&](int i, int j) __attribute__((always_inline)) {
-      const int lr = wm * TM + 32 * i + lrow;
-      const int64_t pos = m0 + (lr < mrows ? lr : 0);
-      const uint16_t* hrow = g.Hs + pos * g.ldh + n0 + b_row(j) + 8 * h;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        hg[j][c] = *(const uint4*)(hrow + 16 * c);  // cached: the block's other loads share these lines
-        hu[j][c] = *(const uint4*)(hrow + g.f + 16 * c);
-      }
-    };
-#pragma unroll
-    for (int j = 0; j < FN; ++j) load_h(0, j);
+    // consecutive.
+    // H and dH move through the LDS slots as whole rows (dact_h_dma above): row block i's H
+    // arrives while block i-1 is computed and stored, and dH leaves by buffer stores whose
+    // bounds (the tile's valid rows) drop the rows past the expert's end.  Every wave that has
+    // rows issues EP_Q DMA and EP_Q store instructions per block, so the waits below count
+    // exactly the vector-memory instructions issued after the awaited DMA.
+    // Every wave is past the last k step's LDS reads: the stage it read is free.
+    asm volatile("s_barrier" ::: "memory");
+    const __amdgpu_buffer_rsrc_t dst =
+        __builtin_amdgcn_make_buffer_rsrc(g.C0 + (int64_t)m0 * g.ldc0, 0, (int)(mrows * g.ldc0 * 2), 0x00020000);
+    if (busy) dact_h_dma(1, (nk + 1) % S);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if (!busy) break;  // uniform
+      const uint32_t slot = lds0 + ((nk + i) % S) * STAGE + wave * EP_SLOT;
+      if (i == 0) vm_wait<EP_Q>();             // then: block 1's DMA
+      else if (i < FM - 1) vm_wait<2 * EP_Q>();  // then: block i-1's stores, block i+1's DMA
+      else vm_wait<EP_Q>();                     // then: block i-1's stores
       const int lr = wm * TM + 32 * i + lrow;
-      const bool ok = lr < mrows;
       const float w = s_w[lr];
-      const int64_t pos = m0 + lr;
       float part = 0.0f;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -504,10 +533,13 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
           }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          uint32_t dg[4], du[4];
+          // the lane's 8 columns: chunk 4j + 2c + h of the wave's TN gate (up) columns
+          const uint32_t ag = slot + km_off<TN>(lrow, 4 * j + 2 * c + h), au = ag + EP_HALF;
+          const u32x4 hgv = *(const LDS_AS u32x4*)(uintptr_t)ag, huv = *(const LDS_AS u32x4*)(uintptr_t)au;
+          u32x4 dg, du;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const uint32_t wg = word_of(hg[j][c], t), wu = word_of(hu[j][c], t);
+            const uint32_t wg = hgv[t], wu = huv[t];
             float r0, r1, s0, s1;
             {
               const float gv = lo_bf16(wg), uv = lo_bf16(wu), Gv = G[8 * c + 2 * t];
@@ -526,16 +558,29 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
             dg[t] = pack_bf16x2(r0, r1);
             du[t] = pack_bf16x2(s0, s1);
           }
-          if (ok) {
-            uint16_t* drow = g.C0 + pos * g.ldc0 + n0 + b_row(j) + 8 * h + 16 * c;
-            *(uint4*)drow = make_uint4(dg[0], dg[1], dg[2], dg[3]);
-            *(uint4*)(drow + g.f) = make_uint4(du[0], du[1], du[2], du[3]);
-          }
+          // dH in place of the H it came from (the wave's LDS operations run in order)
+          *(LDS_AS u32x4*)(uintptr_t)ag = dg;
+          *(LDS_AS u32x4*)(uintptr_t)au = du;
         }
-        if (i + 1 < FM) load_h(i + 1, j);
       }
       part += __shfl_xor(part, 32, 64);  // lanes l and l+32 hold the same row
       if (h == 0) s_part[wn][lr] = part;
+      // the block's dH rows, whole lines per instruction
+      {
+        const int rl = lane / EP_CPR, cc = lane % EP_CPR;
+#pragma unroll
+        for (int q = 0; q < EP_Q; ++q) {
+          const int half = q / EP_QH, r = EP_RPI * (q % EP_QH) + rl;
+          const u32x4 v = *(const LDS_AS u32x4*)(uintptr_t)(slot + half * EP_HALF + km_off<TN>(r, cc));
+          const int lr2 = wm * TM + 32 * i + r;
+          const int col = half * g.f + n0 + wn * TN + 8 * cc;
+          __builtin_amdgcn_raw_buffer_store_b128(v, dst, (int)((lr2 * g.ldc0 + col) * 2), 0, 0);
+        }
+      }
+      if (i + 2 < FM) {
+        lds_wait();  // the slot's reads are done before the DMA refills it
+        dact_h_dma(i + 2, (nk + i) % S);
+      }
     }
     __syncthreads();
     for (int r = tid; r < BM; r += NTH) {
@@ -606,7 +651,7 @@ hipError_t run(const GemmArgs& g, int bm, int bn, dim3 grid, hipStream_t st) {
   else if (bm == 256 && bn == 128)
     grouped_gemm_kernel<MODE, 256, 128, (MODE == M_UP ? 2 : 4), 1, BKC><<<grid, (MODE == M_UP ? 256 : 512), 0, st>>>(g);
   else if ((MODE == M_WG || MODE == M_WG1) && bm == 128 && bn == 256)
-    grouped_gemm_kernel<MODE, 128, 256, 4, 1, BKC><<<grid, 512, 0, st>>>(g);
+    grouped_gemm_kernel<(MODE == M_WG || MODE == M_WG1) ? MODE : M_WG, 128, 256, 4, 1, BKC><<<grid, 512, 0, st>>>(g);
   else if (MODE != M_DACT && bm == 128 && bn == 128)
     grouped_gemm_kernel<MODE == M_DACT ? M_DOWN : MODE, 128, 128, 2, 2, 32><<<grid, 256, 0, st>>>(g);
   else

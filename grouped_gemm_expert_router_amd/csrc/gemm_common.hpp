@@ -61,6 +61,16 @@ __device__ __forceinline__ void vm_lgkm_wait_barrier() {
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
 
+// This wave's vector-memory instructions (loads, LDS DMA and stores, retired in issue order)
+// down to at most N outstanding; no barrier.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// This wave's LDS operations (and scalar loads) complete; no barrier.
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -81,9 +91,13 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 //       group, lane s supplies the address of (k = k0 + s/4, col = c0 + 4*(s%4)) and lane i
 //       receives the 4 values (k0..k0+3, c0 + i).
 template <int BK>
+__device__ __forceinline__ int km_swz(int row) {
+  if constexpr (BK == 32) return (row >> 2) & 3;
+  else return (row >> 1) & 7;
+}
+template <int BK>
 __device__ __forceinline__ uint32_t km_off(int row, int c) {
-  if constexpr (BK == 32) return row * 64 + ((c ^ ((row >> 2) & 3)) << 4);
-  else return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+  return row * (2 * BK) + ((c ^ km_swz<BK>(row)) << 4);
 }
 template <int C>
 __device__ __forceinline__ uint32_t kn_off(int kr, int col) {
