@@ -42,7 +42,10 @@ __device__ __forceinline__ void store_once16(void* p, const uint4& v) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ float sigmoidf_fast(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic sigmoid with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp
+// each) instead of an IEEE division, whose scale/fixup sequence cost ten VALU instructions per
+// element in the SwiGLU epilogues.  z -> -inf gives 1/inf = 0.
+__device__ __forceinline__ float sigmoidf_fast(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
