@@ -45,7 +45,6 @@ struct GemmArgs {
   const int32_t* tokrow;  // ragged K: token row of each sorted position (perm[pos] / k)
   const int2* tiles;
   const int32_t* ntiles;
-  int gatherA, gatherB;  // operand rows come from token perm[pos] / k instead of position pos
   const float* topk_w;
   uint16_t* C0;
   int64_t ldc0;
@@ -93,6 +92,9 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   constexpr bool RAGGED_K = (MODE == M_WG || MODE == M_WG1);
   constexpr bool A_KN = RAGGED_K;                              // A stored [k][m]
   constexpr bool B_KN = !(MODE == M_DACT || MODE == M_DX);     // B stored [k][n]
+  // operand rows that come from token perm[pos] / k instead of sorted position pos: x (UP, dW1)
+  // and dy (dA, dW2)
+  constexpr bool GA = (MODE == M_UP || MODE == M_DACT || MODE == M_WG1), GB = (MODE == M_WG);
   static_assert(MODE != M_UP || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
   constexpr int QA = BM * BK / (512 * NW), QB = BN * BK / (512 * NW);  // DMA instrs per thread per tile
@@ -178,23 +180,15 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     const int lid = xcd_remap(blockIdx.x, G_valid);
     const int2 rc = grouped_tile(lid, G_valid / nN, nN, nN < 8 ? 1 : GEMM_GM);
     nt = rc.y;
-    const int2 te = g.tiles[rc.x];
-    e = te.x;
-    m0 = g.offsets[e] + te.y * BM;
-    mrows = min(BM, g.offsets[e + 1] - m0);
+    // uniform loads through the scalar cache (the tile table and offsets are read-only here)
+    const CONST_AS int32_t* tp = (const CONST_AS int32_t*)g.tiles;
+    e = tp[2 * rc.x];
+    const CONST_AS int32_t* off4 = (const CONST_AS int32_t*)g.offsets;
+    m0 = off4[e] + tp[2 * rc.x + 1] * BM;
+    mrows = min(BM, off4[e + 1] - m0);
     n0 = (MODE == M_UP) ? nt * (BN / 2) : nt * BN;
     kbeg = 0;
     kend = g.K;
-    for (int r = tid; r < BM; r += NTH) {
-      int p = -1;
-      float wv = 0.0f;
-      if (r < mrows) {
-        p = g.perm[m0 + r];
-        if (MODE == M_UP || MODE == M_DACT) wv = g.topk_w[p];
-      }
-      s_slot[r] = p;
-      s_w[r] = wv;
-    }
   }
   const uint16_t* Bexp = g.B + (RAGGED_K ? 0 : (int64_t)e * g.b_estride);
 
@@ -216,7 +210,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
       // rows past the expert's end read row m0: they only feed accumulator rows the epilogue
       // never stores (an output row depends on its own A row only)
       const int pos = m0 + (row < mrows ? row : 0);
-      const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
+      const int64_t src = GA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
       a_src[q] = g.A + src * g.lda + 8 * c;
     }
   } else {
@@ -256,11 +250,11 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   const int klen = kend - kbeg;
   int tok_first = 0;
   if constexpr (RAGGED_K)
-    if (klen > 0 && (g.gatherA || g.gatherB)) tok_first = ((const CONST_AS int32_t*)g.tokrow)[kbeg];
+    if (klen > 0 && (GA || GB)) tok_first = ((const CONST_AS int32_t*)g.tokrow)[kbeg];
   // Ragged K: the tokens of the wave's KRW k rows of step t, one scalar load.
   auto load_tk = [&](int t) __attribute__((always_inline)) -> i32x8 {
     i32x8 tk = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (RAGGED_K && (g.gatherA || g.gatherB)) {
+    if (RAGGED_K && (GA || GB)) {
       if constexpr (KRW == 8) {
         tk = *(const CONST_AS i32x8*)(g.tokrow + kbeg + t * BK + KRW * wave);
       } else {
@@ -302,11 +296,11 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
       };
 #pragma unroll
       for (int q = 0; q < QA; ++q)
-        dma16(g.A + row_of(a_kr[q], tok_sel(q, 512 / BM, BM / 8), g.gatherA) * g.lda + a_col[q],
+        dma16(g.A + row_of(a_kr[q], tok_sel(q, 512 / BM, BM / 8), GA) * g.lda + a_col[q],
               abase + (wave * QA + q) * 1024);
 #pragma unroll
       for (int q = 0; q < QB; ++q)
-        dma16(g.B + row_of(b_kr[q], tok_sel(q, 512 / BN, BN / 8), g.gatherB) * g.ldb + b_col[q],
+        dma16(g.B + row_of(b_kr[q], tok_sel(q, 512 / BN, BN / 8), GB) * g.ldb + b_col[q],
               bbase + (wave * QB + q) * 1024);
     }
   };
@@ -401,10 +395,24 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   // In an expert's last row tile, a wave whose rows all lie past the expert's end skips its
   // fragment reads and MFMAs (uniform: mrows and wm are); it still issues its DMA share.
   const bool busy = __builtin_amdgcn_readfirstlane(wm * TM < mrows);
-  __syncthreads();  // s_slot / s_w visible; the arena is free
+  // The first stages' DMA goes out before anything else waits on memory (the arena of a new
+  // block is free); the epilogue's per-row slot and routing weight are fetched under it.
 #pragma unroll
   for (int t = 0; t < S - 1; ++t)
     if (t < nk) issue(t, t, load_tk(t));
+  if constexpr (!RAGGED_K) {
+    for (int r = tid; r < BM; r += NTH) {
+      int p = -1;
+      float wv = 0.0f;
+      if (r < mrows) {
+        p = g.perm[m0 + r];
+        if (MODE == M_UP || MODE == M_DACT) wv = g.topk_w[p];
+      }
+      s_slot[r] = p;
+      s_w[r] = wv;
+    }
+  }
+  __syncthreads();  // s_slot / s_w visible
   for (int it = 0; it < nk; ++it) {
     // the tokens of the step refilled below are loaded before the wait, so the scalar load's
     // latency overlaps the DMA wait and the barrier
@@ -689,7 +697,6 @@ hipError_t launch_gemm_up(const MoeShape& s, const uint16_t* x, const uint16_t* 
   GemmArgs g = base_args(s, offsets, perm, tiles, ntiles);
   g.A = x;
   g.lda = s.d;
-  g.gatherA = 1;
   g.B = W1;
   g.ldb = 2 * (int64_t)s.f;
   g.b_estride = (int64_t)s.d * 2 * s.f;
@@ -731,7 +738,6 @@ hipError_t launch_gemm_dact(const MoeShape& s, const uint16_t* dy, const uint16_
   GemmArgs g = base_args(s, offsets, perm, tiles, ntiles);
   g.A = dy;
   g.lda = s.d;
-  g.gatherA = 1;
   g.B = W2;  // row n of W2[e] ([f, d]) is column n of W2[e]^T, contiguous in K = d
   g.ldb = s.d;
   g.b_estride = (int64_t)s.f * s.d;
@@ -895,10 +901,8 @@ hipError_t launch_gemm_dw2(const MoeShape& s, const uint16_t* As, const uint16_t
   g.partial = sp.partial;
   g.A = As;
   g.lda = s.f;
-  g.gatherA = 0;
   g.B = dy;
   g.ldb = s.d;
-  g.gatherB = 1;
   g.Mo = s.f;
   g.N = s.d;
   g.C0 = dW2;
@@ -918,10 +922,8 @@ hipError_t launch_gemm_dw1(const MoeShape& s, const uint16_t* x, const uint16_t*
   g.partial = sp.partial;
   g.A = x;
   g.lda = s.d;
-  g.gatherA = 1;
   g.B = dH;
   g.ldb = 2 * (int64_t)s.f;
-  g.gatherB = 0;
   g.Mo = s.d;
   g.N = 2 * s.f;
   g.C0 = dW1;
