@@ -308,15 +308,23 @@ def summarize_counters(fetch_dir, write_dir, config, command):
 
 def summarize_mfma(d, config, command):
     """MFMA pipe utilisation per kernel: SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs)
-    over 1024 x the kernel's cycles per XCD (GRBM_GUI_ACTIVE is summed over the 8 XCDs)."""
+    over 1024 x the kernel's cycles per XCD (GRBM_GUI_ACTIVE is summed over the 8 XCDs).  The
+    kernel's average clock is those cycles over the dispatch's duration, and busy x clock x
+    1024 SIMDs x 1024 flop per SIMD cycle (dense bf16; 2048 for fp8) is the rate the counters
+    imply."""
     acc = {}
     for r in _csv_rows(d, "counter_collection.csv"):
         acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            acc[r["Kernel_Name"]].setdefault("_clock", []).append(float(r["Counter_Value"]) / 8.0 / dur)
     print(f"# rocprofv3 MFMA utilisation per dispatch: {workload_name(config)}")
     print(f"command: {command}")
     print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
-    print("# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); medians over dispatches")
-    print(f"{'stage':<12} {'mfma_busy':>9} {'mfma_insts':>12} {'lds_bank_conf/cu_cyc':>21}  kernel")
+    print("# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); clock = GRBM_GUI_ACTIVE / 8 "
+          "/ dispatch duration; implied = busy x clock x 1024 SIMDs x flop per SIMD cycle; medians over dispatches")
+    print(f"{'stage':<12} {'mfma_busy':>9} {'clock_GHz':>9} {'implied_TF':>10} {'mfma_insts':>12} "
+          f"{'lds_bank_conf/cu_cyc':>21}  kernel")
     med = lambda v: sorted(v)[len(v) // 2]
     for name, c in sorted(acc.items()):
         st = _stage_of(name, config)
@@ -326,7 +334,11 @@ def summarize_mfma(d, config, command):
         busy = med(c["SQ_VALU_MFMA_BUSY_CYCLES"]) / (1024.0 * cyc)
         bc = med(c["SQ_LDS_BANK_CONFLICT"]) / (256.0 * cyc) if "SQ_LDS_BANK_CONFLICT" in c else float("nan")
         ins = med(c["SQ_INSTS_MFMA"]) if "SQ_INSTS_MFMA" in c else float("nan")
-        print(f"{st:<12} {busy:>9.3f} {ins:>12.4g} {bc:>21.4f}  {name.split('(')[0].replace('void ', '')}")
+        clk = med(c["_clock"])
+        fpc = 2048.0 if ("fp8" in name or "_mx_" in name) else 1024.0  # dense flop per SIMD cycle
+        implied = busy * clk * 1024.0 * fpc / 1e12
+        print(f"{st:<12} {busy:>9.3f} {clk / 1e9:>9.3f} {implied:>10.0f} {ins:>12.4g} {bc:>21.4f}  "
+              f"{name.split('(')[0].replace('void ', '')}")
 
 
 # ------------------------------------------------------------------ benchmark
