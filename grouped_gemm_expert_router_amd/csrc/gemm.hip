@@ -20,7 +20,8 @@
 // memory straight into LDS (global_load_lds_dwordx4), in their global orientation, with a
 // 16-byte-chunk XOR swizzle: a K-contiguous tile is read as one ds_read_b128 per MFMA operand,
 // an M- or N-contiguous one with the gfx950 transpose read ds_read_b64_tr_b16.  Two LDS stages:
-// the DMA of k step t+1 is in flight during step t's MFMAs.  Epilogues store from registers.
+// the DMA of k step t+1 is in flight during step t's MFMAs.  Epilogues store from registers,
+// except the dSwiGLU one, which moves H and dH through the freed operand stages as whole rows.
 #include "common.hpp"
 #include "gemm_common.hpp"
 #include "kernels.hpp"
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   constexpr int DPT = QA + QB;
   static_assert(DPT * (S - 2) <= 63 && (BK == 32 || BK == 64), "vmcnt range");
 
-  // LDS: the S operand stages of the K loop (the epilogue stores from registers).
+  // LDS: the S operand stages of the K loop (reused by the dA epilogue for H and dH).
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
   __shared__ float s_w[RAGGED_K ? 1 : BM];
   __shared__ int s_slot[RAGGED_K ? 1 : BM];
