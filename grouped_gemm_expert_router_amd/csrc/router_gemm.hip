@@ -168,6 +168,301 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const RouterArgs g) {
   }
 }
 
+// ---------------------------------------------------------------- E = 128 or 256
+// With the gate's row a whole number of 16-byte chunks and E at most 256, each block owns whole
+// rows of the output along E and its operands reach LDS by DMA (global_load_lds_dwordx4) in the
+// layouts of the grouped GEMMs: K-contiguous tiles read with ds_read_b128 (KM), N- or
+// M-contiguous ones with the transpose read (KN).  These products are bound by HBM (x, dx) and
+// L2 (the gate and d_logits, re-read by every block), so the tiles favour bytes in flight over
+// MFMA efficiency.  4 waves, 2 x 2.
+
+// logits[T, E] = x . Wg: 64 token rows x all E columns per block, 3 stages of BK (128, or 64 for
+// E = 256) along d.  Stage: x rows as BK/64 KM sub-tiles of 64 x 64, then Wg's BK rows (KN, E wide).
+template <int EP>
+__global__ __launch_bounds__(256, 1) void router_logits_fast_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ Wg, int T, int d,
+                                                                   float* __restrict__ logits) {
+  constexpr int BM = 64, BK = EP == 256 ? 64 : 128, S = 3;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * EP * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int QA = A_BYTES / 4096, QB = B_BYTES / 4096, DPT = QA + QB;  // 1 KiB DMAs per wave
+  constexpr int FN = EP / 64, RB = 512 / EP, CHB = EP / 8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
+  const int m0 = blockIdx.x * BM;
+
+  const uint16_t* a_src[QA];
+  const uint16_t* b_src[QB];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int gi = wave * QA + q, h = gi / 8, row = 8 * (gi % 8) + lane / 8;
+    const int c = (lane % 8) ^ km_swz<64>(row);
+    a_src[q] = x + (int64_t)min(m0 + row, T - 1) * d + 64 * h + 8 * c;  // rows past T feed unstored outputs
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int gi = wave * QB + q, kr = RB * gi + lane / CHB;
+    const int c = (lane % CHB) ^ (4 * (kr & 3));
+    b_src[q] = Wg + (int64_t)kr * EP + 8 * c;
+  }
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) dma16(a_src[q] + t * BK, abase + (wave * QA + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) dma16(b_src[q] + (int64_t)t * BK * EP, bbase + (wave * QB + q) * 1024);
+  };
+  f32x16_t acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+
+  const int nk = d / BK;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  for (int it = 0; it < nk; ++it) {
+    if (it + 1 < nk) vm_wait_barrier<DPT>();
+    else vm_wait_barrier<0>();
+    if (it + 2 < nk) issue(it + 2, (it + 2) % S);
+    const uint32_t abase = lds0 + (it % S) * STAGE, bbase = abase + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const bf16x8_t af = read_km<64>(abase + (kk / 4) * 8192, wm * 32 + (lane & 31), 2 * (kk % 4) + (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const bf16x8_t bv = read_kn<EP>(bbase, wn * (EP / 2) + 32 * j, kk, lane);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, af, acc[j], 0, 0, 0);
+      }
+    }
+  }
+  // lane l holds token row l % 32 of the wave's rows and, per block j, columns 8 (r / 4) +
+  // 4 (l / 32) + r % 4
+  const int row = m0 + wm * 32 + (lane & 31);
+  if (row < T) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * (EP / 2) + 32 * j + 8 * q + 4 * (lane >> 5);
+        *(float4*)(logits + (int64_t)row * EP + col) =
+            make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
+      }
+  }
+}
+
+// dx[T, d] += d_logits[T, E] . Wg^T: 64 token rows x BN columns of d per block, the whole K = E at
+// once.  d_logits rows are rounded to bf16 through registers into KM sub-tiles of 64 x 64; the
+// gate's rows n0.. (K-contiguous: row i holds E values) arrive by DMA as KM sub-tiles of BN x 64.
+// The sum with dx is taken in fp32 and rounded once.
+template <int EP>
+__global__ __launch_bounds__(256) void router_dx_fast_kernel(const float* __restrict__ dl,
+                                                            const uint16_t* __restrict__ Wg, int T, int d,
+                                                            uint16_t* __restrict__ dx) {
+  constexpr int BM = 64, BN = EP == 256 ? 128 : 256, KS = EP / 64;
+  constexpr int A_SUB = BM * 128, B_SUB = BN * 128;  // bytes of one 64-deep sub-tile
+  constexpr int QB = KS * B_SUB / 4096;
+  constexpr int FN = BN / 64;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[KS * (A_SUB + B_SUB)];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
+  const uint32_t bbase0 = lds0 + KS * A_SUB;
+  const int nblk = d / BN;
+  const int m0 = (blockIdx.x / nblk) * BM, n0 = (blockIdx.x % nblk) * BN;
+  // the gate's rows by DMA: instruction gi covers sub-tile gi / (B_SUB / 1024), rows 8 (gi %
+  // (B_SUB / 1024)) + lane / 8
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int gi = wave * QB + q, h = gi / (B_SUB / 1024), row = 8 * (gi % (B_SUB / 1024)) + lane / 8;
+    const int c = (lane % 8) ^ km_swz<64>(row);
+    dma16(Wg + (int64_t)(n0 + row) * EP + 64 * h + 8 * c, bbase0 + gi * 1024);
+  }
+  // d_logits rows: thread -> row tid / 4, 16 k values (EP = 128: two chunks) per sub-tile pass
+#pragma unroll
+  for (int h = 0; h < KS; ++h) {
+    const int row = tid >> 2, kc = 16 * (tid & 3);
+    const int t = m0 + row;
+    uint32_t w[8];
+    if (t < T) {
+      const float4* p = (const float4*)(dl + (int64_t)t * EP + 64 * h + kc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = p[i];
+        w[2 * i] = pack_bf16x2(v.x, v.y);
+        w[2 * i + 1] = pack_bf16x2(v.z, v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = 0u;
+    }
+    const uint32_t ab = lds0 + h * A_SUB;
+    *(LDS_AS u32x4*)(uintptr_t)(ab + km_off<64>(row, kc / 8)) = u32x4{w[0], w[1], w[2], w[3]};
+    *(LDS_AS u32x4*)(uintptr_t)(ab + km_off<64>(row, kc / 8 + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+  }
+  vm_wait_barrier<0>();
+  lds_barrier();
+  f32x16_t acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < EP / 16; ++kk) {
+    const bf16x8_t af = read_km<64>(lds0 + (kk / 4) * A_SUB, wm * 32 + (lane & 31), 2 * (kk % 4) + (lane >> 5));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const bf16x8_t bv =
+          read_km<64>(bbase0 + (kk / 4) * B_SUB, wn * (BN / 2) + 32 * j + (lane & 31), 2 * (kk % 4) + (lane >> 5));
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, af, acc[j], 0, 0, 0);
+    }
+  }
+  // half-wave exchange: then acc[j][8c + e] is column 16c + 8h + e of block j (h = lane / 32)
+  const int h = lane >> 5;
+  const int t = m0 + wm * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    f32x16_t& G = acc[j];
+#pragma unroll
+    for (int a = 0; a < 16; a += 8)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(G[a + u]), __float_as_uint(G[a + 4 + u]), false,
+                                                         false);
+        G[a + u] = __uint_as_float(r[0]);
+        G[a + 4 + u] = __uint_as_float(r[1]);
+      }
+    if (t < T) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint16_t* p = dx + (int64_t)t * d + n0 + wn * (BN / 2) + 32 * j + 16 * c + 8 * h;
+        const uint4 o = *(const uint4*)p;
+        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+        uint32_t nw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          nw[u] = pack_bf16x2(lo_bf16(ow[u]) + G[8 * c + 2 * u], hi_bf16(ow[u]) + G[8 * c + 2 * u + 1]);
+        *(uint4*)p = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+      }
+    }
+  }
+}
+
+// dWg[d, E] = x^T . d_logits over one slice of the token axis: 128 rows of d x all E columns per
+// block, 64 tokens per step, 2 stages.  x's token rows (128 columns each, M-contiguous) arrive by
+// DMA as a KN tile; d_logits rows are rounded to bf16 through registers, one step ahead, into a
+// KN tile.  Tokens past the slice (or T) get zero d_logits.  fp32 partials per slice, or dWg in
+// bf16 directly when there is one slice.
+template <int EP>
+__global__ __launch_bounds__(256, 1) void router_dwg_fast_kernel(const uint16_t* __restrict__ x,
+                                                                const float* __restrict__ dl, int T, int d, int kslice,
+                                                                float* __restrict__ partial,
+                                                                uint16_t* __restrict__ dWg) {
+  constexpr int BM = 128, BK = 64, S = 2;
+  constexpr int A_BYTES = BK * BM * 2, B_BYTES = BK * EP * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int QA = A_BYTES / 4096;
+  constexpr int FM = 2, FN = EP / 64;
+  constexpr int BV = BK * EP / 256 / 4;  // float4 loads of d_logits per thread per step
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
+  const int nblk = d / BM;
+  const int i0 = (blockIdx.x % nblk) * BM, slice = blockIdx.x / nblk;
+  const int kbeg = slice * kslice, kend = min(T, kbeg + kslice);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  // x: instruction gi covers token rows 4 gi .. 4 gi + 3 (256-byte rows of 16 chunks)
+  auto issue_a = [&](int t, int st) __attribute__((always_inline)) {
+    const uint32_t abase = lds0 + st * STAGE;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int gi = wave * QA + q, kr = 4 * gi + lane / 16;
+      const int c = (lane % 16) ^ (4 * (kr & 3));
+      const int tok = min(kbeg + t * BK + kr, T - 1);  // past the slice: zero d_logits rows
+      dma16(x + (int64_t)tok * d + i0 + 8 * c, abase + gi * 1024);
+    }
+  };
+  // d_logits: float4 u of thread tid is element 4 (256 u + tid) of the 64 x E tile, row-major
+  auto load_b = [&](int t, float4 (&v)[BV]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+      const int e4 = u * 256 + tid;  // float4 index within the 64 x EP tile
+      const int kr = e4 / (EP / 4), col = 4 * (e4 % (EP / 4));
+      const int tok = kbeg + t * BK + kr;
+      v[u] = tok < kend ? *(const float4*)(dl + (int64_t)tok * EP + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_b = [&](int st, const float4 (&v)[BV]) __attribute__((always_inline)) {
+    const uint32_t bbase = lds0 + st * STAGE + A_BYTES;
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+      const int e4 = u * 256 + tid;
+      const int kr = e4 / (EP / 4), col = 4 * (e4 % (EP / 4));
+      *(LDS_AS u32x2*)(uintptr_t)(bbase + kn_off<EP>(kr, col)) =
+          u32x2{pack_bf16x2(v[u].x, v[u].y), pack_bf16x2(v[u].z, v[u].w)};
+    }
+  };
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  float4 bvv[BV];
+  if (nk > 0) {
+    issue_a(0, 0);
+    load_b(0, bvv);
+  }
+  for (int it = 0; it < nk; ++it) {
+    const int st = it % S;
+    store_b(st, bvv);
+    vm_wait_barrier<0>();
+    lds_barrier();
+    if (it + 1 < nk) {  // the next step's operands are in flight during this step's MFMAs
+      issue_a(it + 1, (it + 1) % S);
+      load_b(it + 1, bvv);
+    }
+    const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t af[FM], bv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = read_kn<BM>(abase, wm * 64 + 32 * i, kk, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bv[j] = read_kn<EP>(bbase, wn * (EP / 2) + 32 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], af[i], acc[i][j], 0, 0, 0);
+    }
+    lds_barrier();  // every wave is done with this stage before the next refill
+  }
+  // lane l holds row i0 + wm 64 + 32 i + l % 32 of dWg and, per block j, columns 8 (r / 4) +
+  // 4 (l / 32) + r % 4
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = i0 + wm * 64 + 32 * i + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * (EP / 2) + 32 * j + 8 * q + 4 * (lane >> 5);
+        if (partial) {
+          *(float4*)(partial + ((int64_t)slice * d + row) * EP + col) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        } else {
+          *(u32x2*)(dWg + (int64_t)row * EP + col) =
+              u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]), pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+        }
+      }
+  }
+}
+
 // dWg = bf16(sum over slices, in slice order, of the fp32 partials).
 __global__ __launch_bounds__(256) void router_dwg_reduce_kernel(const float* __restrict__ partial, int64_t n,
                                                                 int slices, uint16_t* __restrict__ dWg) {
@@ -215,8 +510,18 @@ size_t router_ws_bytes(int64_t T, int d, int E) {
   return s > 1 ? (size_t)s * d * E * sizeof(float) : 0;
 }
 
+// The E = 128 / 256 kernels' shape rules (d is a multiple of 128 for every layer; 16-byte
+// alignment of x, Wg, d_logits and dx is checked at the boundary).
+static bool router_fast(int E) { return E == 128 || E == 256; }
+
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wg, int T, int d, int E, float* logits,
                                 hipStream_t st) {
+  if (router_fast(E) && T > 0) {
+    const unsigned grid = (unsigned)((T + 63) / 64);
+    if (E == 128) router_logits_fast_kernel<128><<<grid, 256, 0, st>>>(x, Wg, T, d, logits);
+    else router_logits_fast_kernel<256><<<grid, 256, 0, st>>>(x, Wg, T, d, logits);
+    return hipGetLastError();
+  }
   RouterArgs g{};
   g.A = x;
   g.lda = d;
@@ -235,6 +540,13 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wg, int T, in
 
 hipError_t launch_router_dx(const float* d_logits, const uint16_t* Wg, int T, int d, int E, uint16_t* dx,
                             hipStream_t st) {
+  const int bn = E == 256 ? 128 : 256;
+  if (router_fast(E) && T > 0 && d % bn == 0) {
+    const unsigned grid = (unsigned)((int64_t)(T + 63) / 64 * (d / bn));
+    if (E == 128) router_dx_fast_kernel<128><<<grid, 256, 0, st>>>(d_logits, Wg, T, d, dx);
+    else router_dx_fast_kernel<256><<<grid, 256, 0, st>>>(d_logits, Wg, T, d, dx);
+    return hipGetLastError();
+  }
   RouterArgs g{};
   g.A = d_logits;  // [T, E]: (m = t, k = e)
   g.lda = E;
@@ -255,6 +567,17 @@ hipError_t launch_router_dwg(const uint16_t* x, const float* d_logits, int T, in
                              float* partial, hipStream_t st) {
   int slices, kslice;
   router_dwg_split(T, d, E, &slices, &kslice);
+  if (router_fast(E) && T > 0) {
+    float* part = slices > 1 ? partial : nullptr;
+    const unsigned grid = (unsigned)((d / 128) * slices);
+    if (E == 128) router_dwg_fast_kernel<128><<<grid, 256, 0, st>>>(x, d_logits, T, d, kslice, part, dWg);
+    else router_dwg_fast_kernel<256><<<grid, 256, 0, st>>>(x, d_logits, T, d, kslice, part, dWg);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || slices == 1) return e;
+    const int64_t n = (int64_t)d * E;
+    router_dwg_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(partial, n, slices, dWg);
+    return hipGetLastError();
+  }
   RouterArgs g{};
   g.A = x;         // (m = i, k = t) at x[t*d + i]
   g.lda = d;
