@@ -253,102 +253,117 @@ __global__ __launch_bounds__(256, 1) void router_logits_fast_kernel(const uint16
   }
 }
 
-// dx[T, d] += d_logits[T, E] . Wg^T: 64 token rows x BN columns of d per block, the whole K = E at
-// once.  d_logits rows are rounded to bf16 through registers into KM sub-tiles of 64 x 64; the
-// gate's rows n0.. (K-contiguous: row i holds E values) arrive by DMA as KM sub-tiles of BN x 64.
-// The sum with dx is taken in fp32 and rounded once.
+// dx[T, d] += d_logits[T, E] . Wg^T.  A block owns 128 columns of d: the gate's rows n0 ..
+// n0 + BN - 1 (K-contiguous: row i holds its E values) arrive once by DMA as KM sub-tiles of
+// BN x 64 and stay in LDS while the block walks its 64-row token tiles (every rgroups-th tile).
+// Per tile, d_logits rows are rounded to bf16 through registers (loaded one tile ahead) into KM
+// sub-tiles of 64 x 64, the product takes the whole K = E at once, and the sum with dx (whose
+// rows are loaded before the MFMAs) is taken in fp32 and rounded once.
 template <int EP>
-__global__ __launch_bounds__(256) void router_dx_fast_kernel(const float* __restrict__ dl,
-                                                            const uint16_t* __restrict__ Wg, int T, int d,
-                                                            uint16_t* __restrict__ dx) {
-  constexpr int BM = 64, BN = EP == 256 ? 128 : 256, KS = EP / 64;
+__global__ __launch_bounds__(256, EP == 128 ? 2 : 1) void router_dx_fast_kernel(const float* __restrict__ dl,
+                                                                               const uint16_t* __restrict__ Wg,
+                                                                               int T, int d, int rgroups,
+                                                                               uint16_t* __restrict__ dx) {
+  constexpr int BM = 64, BN = 128, KS = EP / 64;
   constexpr int A_SUB = BM * 128, B_SUB = BN * 128;  // bytes of one 64-deep sub-tile
-  constexpr int QB = KS * B_SUB / 4096;
-  constexpr int FN = BN / 64;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[KS * (A_SUB + B_SUB)];
+  constexpr int A_BYTES = KS * A_SUB, QB = KS * B_SUB / 4096;
+  constexpr int FN = BN / 64, NV = BM * EP / 4 / 256;  // float4 of d_logits per thread per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[KS * B_SUB + 2 * A_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
-  const uint32_t bbase0 = lds0 + KS * A_SUB;
+  const uint32_t bbase = lds0, abase0 = lds0 + KS * B_SUB;
   const int nblk = d / BN;
-  const int m0 = (blockIdx.x / nblk) * BM, n0 = (blockIdx.x % nblk) * BN;
-  // the gate's rows by DMA: instruction gi covers sub-tile gi / (B_SUB / 1024), rows 8 (gi %
-  // (B_SUB / 1024)) + lane / 8
+  const int n0 = (blockIdx.x % nblk) * BN, rg = blockIdx.x / nblk;
+  const int ntile = (T + BM - 1) / BM;
+  // the gate's rows by DMA: instruction gi covers sub-tile gi / (B_SUB / 1024), rows
+  // 8 (gi % (B_SUB / 1024)) + lane / 8
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
     const int gi = wave * QB + q, h = gi / (B_SUB / 1024), row = 8 * (gi % (B_SUB / 1024)) + lane / 8;
     const int c = (lane % 8) ^ km_swz<64>(row);
-    dma16(Wg + (int64_t)(n0 + row) * EP + 64 * h + 8 * c, bbase0 + gi * 1024);
+    dma16(Wg + (int64_t)(n0 + row) * EP + 64 * h + 8 * c, bbase + gi * 1024);
   }
-  // d_logits rows: thread -> row tid / 4, 16 k values (EP = 128: two chunks) per sub-tile pass
+  // d_logits of token tile rt: float4 u of thread tid is element 4 (256 u + tid) of the 64 x E
+  // tile, row-major; rows past T are zero
+  auto load_dl = [&](int rt, float4 (&v)[NV]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int h = 0; h < KS; ++h) {
-    const int row = tid >> 2, kc = 16 * (tid & 3);
-    const int t = m0 + row;
-    uint32_t w[8];
-    if (t < T) {
-      const float4* p = (const float4*)(dl + (int64_t)t * EP + 64 * h + kc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 v = p[i];
-        w[2 * i] = pack_bf16x2(v.x, v.y);
-        w[2 * i + 1] = pack_bf16x2(v.z, v.w);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = 0u;
+    for (int u = 0; u < NV; ++u) {
+      const int e4 = u * 256 + tid, row = e4 / (EP / 4), col = 4 * (e4 % (EP / 4));
+      const int t = rt * BM + row;
+      v[u] = t < T ? *(const float4*)(dl + (int64_t)t * EP + col) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const uint32_t ab = lds0 + h * A_SUB;
-    *(LDS_AS u32x4*)(uintptr_t)(ab + km_off<64>(row, kc / 8)) = u32x4{w[0], w[1], w[2], w[3]};
-    *(LDS_AS u32x4*)(uintptr_t)(ab + km_off<64>(row, kc / 8 + 1)) = u32x4{w[4], w[5], w[6], w[7]};
-  }
-  vm_wait_barrier<0>();
-  lds_barrier();
-  f32x16_t acc[FN];
+  };
+  auto store_dl = [&](uint32_t ab, const float4 (&v)[NV]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < FN; ++j)
+    for (int u = 0; u < NV; ++u) {
+      const int e4 = u * 256 + tid, row = e4 / (EP / 4), col = 4 * (e4 % (EP / 4));
+      const uint32_t a = ab + (col / 64) * A_SUB + km_off<64>(row, (col % 64) / 8) + 2 * (col % 8);
+      *(LDS_AS u32x2*)(uintptr_t)a = u32x2{pack_bf16x2(v[u].x, v[u].y), pack_bf16x2(v[u].z, v[u].w)};
+    }
+  };
+  const int h = lane >> 5;
+  float4 v[NV];
+  if (rg < ntile) load_dl(rg, v);
+  for (int rt = rg, i = 0; rt < ntile; rt += rgroups, ++i) {
+    const uint32_t ab = abase0 + (i & 1) * A_BYTES;
+    store_dl(ab, v);
+    if (i == 0) vm_wait<0>();  // this wave's DMA of the gate
+    lds_barrier();             // the tile (and the gate) visible to every wave
+    if (rt + rgroups < ntile) load_dl(rt + rgroups, v);  // next tile, under this one's work
+    // this lane's dx values: block j, half c: row t, columns 16c + 8h .. + 7 of the block
+    const int t = rt * BM + wm * 32 + (lane & 31);
+    uint4 o[FN][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-  for (int kk = 0; kk < EP / 16; ++kk) {
-    const bf16x8_t af = read_km<64>(lds0 + (kk / 4) * A_SUB, wm * 32 + (lane & 31), 2 * (kk % 4) + (lane >> 5));
+      for (int c = 0; c < 2; ++c)
+        o[j][c] = t < T ? *(const uint4*)(dx + (int64_t)t * d + n0 + wn * (BN / 2) + 32 * j + 16 * c + 8 * h)
+                        : make_uint4(0u, 0u, 0u, 0u);
+    f32x16_t acc[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < EP / 16; ++kk) {
+      const bf16x8_t af = read_km<64>(ab + (kk / 4) * A_SUB, wm * 32 + (lane & 31), 2 * (kk % 4) + (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const bf16x8_t bv =
+            read_km<64>(bbase + (kk / 4) * B_SUB, wn * (BN / 2) + 32 * j + (lane & 31), 2 * (kk % 4) + (lane >> 5));
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, af, acc[j], 0, 0, 0);
+      }
+    }
+    // half-wave exchange: then acc[j][8c + e] is column 16c + 8h + e of block j
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const bf16x8_t bv =
-          read_km<64>(bbase0 + (kk / 4) * B_SUB, wn * (BN / 2) + 32 * j + (lane & 31), 2 * (kk % 4) + (lane >> 5));
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, af, acc[j], 0, 0, 0);
-    }
-  }
-  // half-wave exchange: then acc[j][8c + e] is column 16c + 8h + e of block j (h = lane / 32)
-  const int h = lane >> 5;
-  const int t = m0 + wm * 32 + (lane & 31);
+      f32x16_t& G = acc[j];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    f32x16_t& G = acc[j];
+      for (int a = 0; a < 16; a += 8)
 #pragma unroll
-    for (int a = 0; a < 16; a += 8)
+        for (int u = 0; u < 4; ++u) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(G[a + u]), __float_as_uint(G[a + 4 + u]),
+                                                           false, false);
+          G[a + u] = __uint_as_float(r[0]);
+          G[a + 4 + u] = __uint_as_float(r[1]);
+        }
+      if (t < T) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(G[a + u]), __float_as_uint(G[a + 4 + u]), false,
-                                                         false);
-        G[a + u] = __uint_as_float(r[0]);
-        G[a + 4 + u] = __uint_as_float(r[1]);
-      }
-    if (t < T) {
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t ow[4] = {o[j][c].x, o[j][c].y, o[j][c].z, o[j][c].w};
+          uint32_t nw[4];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        uint16_t* p = dx + (int64_t)t * d + n0 + wn * (BN / 2) + 32 * j + 16 * c + 8 * h;
-        const uint4 o = *(const uint4*)p;
-        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
-        uint32_t nw[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          nw[u] = pack_bf16x2(lo_bf16(ow[u]) + G[8 * c + 2 * u], hi_bf16(ow[u]) + G[8 * c + 2 * u + 1]);
-        *(uint4*)p = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+          for (int u = 0; u < 4; ++u)
+            nw[u] = pack_bf16x2(lo_bf16(ow[u]) + G[8 * c + 2 * u], hi_bf16(ow[u]) + G[8 * c + 2 * u + 1]);
+          *(uint4*)(dx + (int64_t)t * d + n0 + wn * (BN / 2) + 32 * j + 16 * c + 8 * h) =
+              make_uint4(nw[0], nw[1], nw[2], nw[3]);
+        }
       }
     }
   }
+  vm_wait<0>();  // a block with no token tile still waits for its DMA before it ends
 }
 
 // dWg[d, E] = x^T . d_logits over one slice of the token axis: 128 rows of d x all E columns per
@@ -540,11 +555,17 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* Wg, int T, in
 
 hipError_t launch_router_dx(const float* d_logits, const uint16_t* Wg, int T, int d, int E, uint16_t* dx,
                             hipStream_t st) {
-  const int bn = E == 256 ? 128 : 256;
+  const int bn = 128;
   if (router_fast(E) && T > 0 && d % bn == 0) {
-    const unsigned grid = (unsigned)((int64_t)(T + 63) / 64 * (d / bn));
-    if (E == 128) router_dx_fast_kernel<128><<<grid, 256, 0, st>>>(d_logits, Wg, T, d, dx);
-    else router_dx_fast_kernel<256><<<grid, 256, 0, st>>>(d_logits, Wg, T, d, dx);
+    // two blocks per compute unit (E = 128) or one: each column slice of d takes rgroups
+    // interleaved groups of token tiles
+    const int nblk = d / bn, ntile = (T + 63) / 64;
+    const int want = E == 128 ? 512 : 256;
+    int rgroups = (want + nblk - 1) / nblk;
+    if (rgroups > ntile) rgroups = ntile;
+    const unsigned grid = (unsigned)(nblk * rgroups);
+    if (E == 128) router_dx_fast_kernel<128><<<grid, 256, 0, st>>>(d_logits, Wg, T, d, rgroups, dx);
+    else router_dx_fast_kernel<256><<<grid, 256, 0, st>>>(d_logits, Wg, T, d, rgroups, dx);
     return hipGetLastError();
   }
   RouterArgs g{};

@@ -26,8 +26,8 @@ CASES = {
     "router_E128_k8": (1000, 512, 256, 128, 8, 52),
     "router_one_token": (1, 128, 128, 4, 2, 53),
     # the E = 128 / 256 kernels: E = 256 with a ragged token count; fewer tokens than one
-    # 64-row block; d not a multiple of 256 (dx then takes the general kernel); token slices of
-    # dWg whose length (224) is not a whole number of 64-token steps
+    # 64-row block; d = 384 (three 128-column slices of dx); token slices of dWg whose length
+    # (224) is not a whole number of 64-token steps
     "router_E256_ragged": (130, 384, 128, 256, 8, 55),
     "router_E128_T33": (33, 256, 128, 128, 4, 56),
     "router_E128_d384": (300, 384, 128, 128, 6, 57),
