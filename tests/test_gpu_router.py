@@ -32,6 +32,8 @@ CASES = {
     "router_E128_T33": (33, 256, 128, 128, 4, 56),
     "router_E128_d384": (300, 384, 128, 128, 6, 57),
     "router_E128_T600": (600, 256, 128, 128, 8, 58),
+    # one token and d = 128: a single x step, a single 128-column slice of dx, one dWg slice
+    "router_E128_one_token": (1, 128, 128, 128, 8, 59),
 }
 
 
