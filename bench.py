@@ -53,7 +53,8 @@ STAGE_KERNEL_BF16 = {"gemm_up": "moe::grouped_gemm_kernel<0,", "gemm_down": "moe
                      "combine": "moe::combine_kernel", "router": "moe::router_topk_kernel",
                      "dlogits": "moe::dlogits_kernel", "wg_reduce": "moe::wg_reduce_kernel",
                      "plan": "moe::plan_", "tile_map": "moe::tile_map_kernel", "wg_split": "moe::wg_split_kernel",
-                     "tokrow": "moe::tokrow_kernel", "permute": "moe::permute_kernel"}
+                     "tokrow": "moe::tokrow_kernel", "permute": "moe::permute_kernel",
+                     "gemm_fused": "moe::fused_forward_kernel", "fwd_queue": "moe::fwd_queue_kernel"}
 # blockwise fp8: the four data GEMMs in e4m3, the weight gradients in bf16 on x dequantised to bf16
 STAGE_KERNEL_FP8 = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_fp8_kernel<0>",
                         gemm_down="moe::grouped_gemm_fp8_kernel<1>", gemm_dact="moe::grouped_gemm_fp8_kernel<2>",
@@ -540,6 +541,39 @@ def main():
                    "frac_hbm_peak": pby / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del xp
 
+    # the single-launch forward (moe_forward_fused: gather, both grouped GEMMs and the SwiGLU in
+    # one persistent launch, then the combine) against the forward of the timed step, on the same
+    # routing, outside the timed region; its output must equal the step's bit for bit
+    fused = None
+    if not fp8 and not mx:
+        y2 = torch.empty_like(b["y"])
+        s2 = torch.empty_like(b["saved"])
+        fwd = lambda: moe.moe_forward(dm, x, None, W1, None, W2, None, b["topk_w"], b["offsets"], b["perm"],
+                                      b["inv_perm"], b["y"], b["saved"], b["ws_fwd"])
+        fus = lambda: moe.moe_forward_fused(dm, x, W1, W2, b["topk_w"], b["offsets"], b["perm"], b["inv_perm"], y2,
+                                            s2, b["ws_fwd"])
+        fwd()
+        fus()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(b["y"].view(torch.int16), y2.view(torch.int16)))
+        f0, f1, f2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        reps = 10
+        f0.record(cur)
+        for _ in range(reps):
+            fwd()
+        f1.record(cur)
+        for _ in range(reps):
+            fus()
+        f2.record(cur)
+        torch.cuda.synchronize()
+        tms, fms = f0.elapsed_time(f1) / reps, f1.elapsed_time(f2) / reps
+        ffl = 6.0 * A * d * f
+        fused = {"fused_ms": fms, "two_launch_ms": tms, "fused_tflops": ffl / (fms * 1e-3) / 1e12,
+                 "two_launch_tflops": ffl / (tms * 1e-3) / 1e12, "y_bitwise_equal": same,
+                 "note": "forward only (queue or tile table, GEMMs, combine); outside the timed step"}
+        log(f"[bench] forward: single launch {fms:.3f} ms, two launches {tms:.3f} ms, equal={same}")
+        del y2, s2
+
     # router front end (the gate in front of the layer; its logits are the step's input, so it is
     # timed here on its own): logits = x Wg, then the backward through it (dWg and dx += dl Wg^T)
     router = None
@@ -607,7 +641,8 @@ def main():
         "frac_of_bf16_peak": tflops / PEAK_TFLOPS["bf16"],
         "frac_of_mfma_peak": ideal_ms / ms,
         "useful_flop_per_step": useful, "ms_per_step_with_stage_events": ms_ev, "stages": stages,
-        "permute_standalone": permute, "router_front_end": router, "roofline": roof,
+        "permute_standalone": permute, "router_front_end": router, "single_launch_forward": fused,
+        "roofline": roof,
         "llc_cold": cold, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -18,8 +18,8 @@ MOE_WS_ROUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD, MOE_WS_ROUTER = 0, 1, 2, 3
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
 
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_saved_bytes", "moe_route", "moe_route_noalloc", "moe_plan",
-                "moe_forward", "moe_backward", "moe_router_logits", "moe_router_backward", "moe_permute",
-                "moe_combine", "moe_mxfp8_quantize", "moe_set_stage_hook", "moe_status_string")
+                "moe_forward", "moe_forward_fused", "moe_backward", "moe_router_logits", "moe_router_backward",
+                "moe_permute", "moe_combine", "moe_mxfp8_quantize", "moe_set_stage_hook", "moe_status_string")
 
 
 class MoeDims(ctypes.Structure):
@@ -60,6 +60,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_route_noalloc.argtypes = [dp] + [vp] * 7 + [vp]
     lib.moe_plan.argtypes = [dp] + [vp] * 6 + [sz, vp]
     lib.moe_forward.argtypes = [dp] + [vp] * 13 + [sz, vp]
+    lib.moe_forward_fused.argtypes = [dp] + [vp] * 10 + [sz, vp]
     lib.moe_backward.argtypes = [dp] + [vp] * 19 + [sz, vp]
     lib.moe_router_logits.argtypes = [dp, vp, vp, vp, vp]
     lib.moe_router_backward.argtypes = [dp] + [vp] * 6 + [sz, vp]
@@ -144,6 +145,13 @@ def moe_forward(dm, x, x_scale, W1, W1_scale, W2, W2_scale, topk_w, offsets, per
     _check("moe_forward", load_library().moe_forward(
         ctypes.byref(dm), _ptr(x), _ptr(x_scale), _ptr(W1), _ptr(W1_scale), _ptr(W2), _ptr(W2_scale), _ptr(topk_w),
         _ptr(offsets), _ptr(perm), _ptr(inv_perm), _ptr(y), _ptr(saved), _ptr(ws), nb, _stream(stream)))
+
+
+def moe_forward_fused(dm, x, W1, W2, topk_w, offsets, perm, inv_perm, y, saved, ws, ws_bytes=None, stream=None):
+    nb = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check("moe_forward_fused", load_library().moe_forward_fused(
+        ctypes.byref(dm), _ptr(x), _ptr(W1), _ptr(W2), _ptr(topk_w), _ptr(offsets), _ptr(perm), _ptr(inv_perm),
+        _ptr(y), _ptr(saved), _ptr(ws), nb, _stream(stream)))
 
 
 def moe_backward(dm, dy, x, x_scale, W1, W1_scale, W2, W2_scale, topk_ids, topk_w, offsets, perm, inv_perm, saved,
@@ -233,7 +241,8 @@ def alloc_layer_buffers(dm: MoeDims, device="cuda", backward: bool = True) -> di
 
 
 __all__ = ["MoeDims", "MoEError", "dims", "load_library", "status_string", "moe_workspace_bytes", "moe_saved_bytes",
-           "moe_route", "moe_route_noalloc", "moe_plan", "moe_forward", "moe_backward", "moe_router_logits",
+           "moe_route", "moe_route_noalloc", "moe_plan", "moe_forward", "moe_forward_fused", "moe_backward",
+           "moe_router_logits",
            "moe_router_backward", "moe_permute", "moe_combine",
            "moe_mxfp8_quantize", "moe_set_stage_hook", "alloc_layer_buffers", "ENTRY_POINTS", "MOE_BF16",
            "MOE_FP8_E4M3", "MOE_MXFP8", "MOE_WS_ROUTE", "MOE_WS_FORWARD",

@@ -409,6 +409,35 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
   return MOE_OK;
 }
 
+int moe_forward_fused(const moe_dims* dims, const void* x, const void* W1, const void* W2, const float* topk_w,
+                      const int32_t* offsets, const int32_t* perm, const int32_t* inv_perm, void* y, void* saved,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (dims->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !W1 || !W2 || !topk_w || !offsets || !perm || !inv_perm || !y || !saved || !ws) return MOE_ERR_NULL;
+  const FwdLayout L = fwd_layout(dims);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!al16(x) || !al16(W1) || !al16(W2) || !al16(y) || !al256p(saved) || !al256p(ws)) return MOE_ERR_ALIGN;
+  const MoeShape s = shape_of(dims);
+  const SavedLayout SL = saved_layout(dims);
+  char* w = (char*)ws;
+  char* sv = (char*)saved;
+  // the forward's tile table and count words hold the work queue and its counters
+  int2* items = (int2*)(w + L.tiles);
+  int32_t* qinfo = (int32_t*)(w + L.ntiles);
+  uint16_t* Op = (uint16_t*)(w + L.op);
+  uint16_t* H = (uint16_t*)(sv + SL.H);
+  uint16_t* As = (uint16_t*)(sv + SL.As);
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("fwd_queue", launch_fwd_queue(s, offsets, items, qinfo, st));
+  MOE_TRY("gemm_fused", launch_fused_forward(s, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W2, topk_w,
+                                             offsets, perm, items, qinfo, H, As, Op, st));
+  MOE_TRY("combine", launch_combine(Op, inv_perm, s.T, s.d, s.k, (uint16_t*)y, st));
+  return MOE_OK;
+}
+
 // MXFP8 weight gradients: dW2 = As^T dy and dW1 = x^T dH with every operand quantised along the
 // token axis in 32-row blocks inside each expert's 128-padded segment.
 static int mx_weight_grads(const MoeShape& s, const BwdLayout& L, char* w, const uint16_t* x, const uint16_t* dy,

@@ -86,39 +86,24 @@ __device__ __forceinline__ void sched_interleave() {
 #define GEMM_GM 8
 #endif
 
-template <int MODE, int BM, int BN, int WN, int OCC, int BK>
-__global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmArgs g) {
-  constexpr int S = BK == 32 ? 4 : 2, WM = 2, NW = WM * WN, NTH = 64 * NW;
-  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+// One output tile: expert e, rows m0 .. m0+mrows-1 of the sorted order (ragged M) or of dW[e]
+// (ragged K), column tile nt starting at n0, reduction over k rows kbeg .. kend-1; ragged K:
+// chunk kchunk of the expert and its first partial slot pslot (-1: the expert is not split).
+struct TileCoord {
+  int e, m0, mrows, n0, nt, kbeg, kend, kchunk, pslot;
+};
+
+// LDS bytes of a tile's operand stages
+template <int BM, int BN, int BK>
+constexpr int tile_lds_bytes() {
+  return (BK == 32 ? 4 : 2) * (BM * BK * 2 + BN * BK * 2);
+}
+
+// The tile of block blockIdx.x in a grid of one block per tile; false for blocks past the tiles
+// that exist (known on the device only).  Uniform over the block.
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ bool tile_coord(const GemmArgs& g, TileCoord& c) {
   constexpr bool RAGGED_K = (MODE == M_WG || MODE == M_WG1);
-  constexpr bool A_KN = RAGGED_K;                              // A stored [k][m]
-  constexpr bool B_KN = !(MODE == M_DACT || MODE == M_DX);     // B stored [k][n]
-  // operand rows that come from token perm[pos] / k instead of sorted position pos: x (UP, dW1)
-  // and dy (dA, dW2)
-  constexpr bool GA = (MODE == M_UP || MODE == M_DACT || MODE == M_WG1), GB = (MODE == M_WG);
-  static_assert(MODE != M_UP || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
-  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
-  constexpr int QA = BM * BK / (512 * NW), QB = BN * BK / (512 * NW);  // DMA instrs per thread per tile
-  constexpr int KRW = BK / NW;                                 // ragged K: k rows per wave's DMA
-  static_assert(QA >= 1 && QB >= 1 && (!RAGGED_K || KRW == 4 || KRW == 8), "tile / wave split");
-  constexpr int DPT = QA + QB;
-  static_assert(DPT * (S - 2) <= 63 && (BK == 32 || BK == 64), "vmcnt range");
-
-  // LDS: the S operand stages of the K loop (reused by the dA epilogue for H and dH).
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
-  __shared__ float s_w[RAGGED_K ? 1 : BM];
-  __shared__ int s_slot[RAGGED_K ? 1 : BM];
-  __shared__ float s_part[MODE == M_DACT ? WN : 1][MODE == M_DACT ? BM : 1];  // DACT: per-wave-column partials
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
-
-  // ------------------------------------------------------------------ tile coordinates
-  // The grid is sized for the worst case; only the first G_valid blocks (known on the device)
-  // have work.  They are spread round-robin over the XCDs, so remapping within G_valid keeps
-  // every XCD equally busy.
   int e, m0, mrows, n0, nt, kbeg, kend;
   int kchunk = 0, pslot = -1;
   if constexpr (RAGGED_K) {
@@ -127,7 +112,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     const CONST_AS int32_t* meta = (const CONST_AS int32_t*)g.wg_meta;
     const int U = meta[0];
     const int G_valid = U * per_u;
-    if ((int)blockIdx.x >= G_valid) return;  // uniform: the block has no work
+    if ((int)blockIdx.x >= G_valid) return false;  // uniform: the block has no work
     // Units come in decreasing size.  Deal them to 8 buckets round-robin (bucket b holds units
     // b, b+8, ...: near-equal work per bucket) and give XCD b the tiles of bucket b, so each
     // XCD streams its units' operand rows from HBM into its own L2 once instead of every XCD
@@ -177,7 +162,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
   } else {
     const int nN = (MODE == M_UP) ? g.f / (BN / 2) : g.N / BN;
     const int G_valid = *(const CONST_AS int32_t*)g.ntiles * nN;
-    if ((int)blockIdx.x >= G_valid) return;  // uniform: the block has no work
+    if ((int)blockIdx.x >= G_valid) return false;  // uniform: the block has no work
     const int lid = xcd_remap(blockIdx.x, G_valid);
     const int2 rc = grouped_tile(lid, G_valid / nN, nN, nN < 8 ? 1 : GEMM_GM);
     nt = rc.y;
@@ -191,6 +176,41 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     kbeg = 0;
     kend = g.K;
   }
+  c = TileCoord{e, m0, mrows, n0, nt, kbeg, kend, kchunk, pslot};
+  return true;
+}
+
+// One BM x BN output tile, computed by the block's NW = 2*WN waves.  smem holds the operand
+// stages (tile_lds_bytes), s_w and s_slot the routing weight and pair of each tile row (ragged
+// M), s_part the dA epilogue's per-wave-column partials ([WN][BM]).  The arena must be free when
+// the tile starts: no wave of the block may still read it.
+template <int MODE, int BM, int BN, int WN, int BK>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const TileCoord& tc, uint8_t* smem, float* s_w,
+                                          int* s_slot, float* s_part) {
+  constexpr int S = BK == 32 ? 4 : 2, WM = 2, NW = WM * WN, NTH = 64 * NW;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr bool RAGGED_K = (MODE == M_WG || MODE == M_WG1);
+  constexpr bool A_KN = RAGGED_K;                              // A stored [k][m]
+  constexpr bool B_KN = !(MODE == M_DACT || MODE == M_DX);     // B stored [k][n]
+  // operand rows that come from token perm[pos] / k instead of sorted position pos: x (UP, dW1)
+  // and dy (dA, dW2)
+  constexpr bool GA = (MODE == M_UP || MODE == M_DACT || MODE == M_WG1), GB = (MODE == M_WG);
+  static_assert(MODE != M_UP || (FN % 2 == 0), "gate/up pairing needs an even fragment count");
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int QA = BM * BK / (512 * NW), QB = BN * BK / (512 * NW);  // DMA instrs per thread per tile
+  constexpr int KRW = BK / NW;                                 // ragged K: k rows per wave's DMA
+  static_assert(QA >= 1 && QB >= 1 && (!RAGGED_K || KRW == 4 || KRW == 8), "tile / wave split");
+  constexpr int DPT = QA + QB;
+  static_assert(DPT * (S - 2) <= 63 && (BK == 32 || BK == 64), "vmcnt range");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr_of(smem));
+  const int e = tc.e, m0 = tc.m0, mrows = tc.mrows, n0 = tc.n0, nt = tc.nt, kbeg = tc.kbeg, kend = tc.kend;
+  const int kchunk = tc.kchunk, pslot = tc.pslot;
+  (void)kchunk;
+  (void)pslot;
   const uint16_t* Bexp = g.B + (RAGGED_K ? 0 : (int64_t)e * g.b_estride);
 
   // ------------------------------------------------------------------ DMA source pointers
@@ -573,7 +593,7 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
         }
       }
       part += __shfl_xor(part, 32, 64);  // lanes l and l+32 hold the same row
-      if (h == 0) s_part[wn][lr] = part;
+      if (h == 0) s_part[wn * BM + lr] = part;
       // the block's dH rows, whole lines per instruction
       {
         const int rl = lane / EP_CPR, cc = lane % EP_CPR;
@@ -593,9 +613,9 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
     }
     __syncthreads();
     for (int r = tid; r < BM; r += NTH) {
-      float sum = s_part[0][r];
+      float sum = s_part[r];
 #pragma unroll
-      for (int c = 1; c < WN; ++c) sum += s_part[c][r];
+      for (int c = 1; c < WN; ++c) sum += s_part[c * BM + r];
       if (r < mrows) g.dwp[(int64_t)nt * g.dwp_stride + m0 + r] = sum;
     }
   } else if (RAGGED_K && pslot >= 0) {
@@ -636,6 +656,141 @@ __global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmA
           *(uint4*)(dst + 16) = hi;
         }
       }
+    }
+  }
+}
+
+// One block per tile; the grid is sized for the worst case and only the first G_valid blocks
+// (known on the device) have work.  They are spread round-robin over the XCDs, so remapping
+// within G_valid keeps every XCD equally busy.
+template <int MODE, int BM, int BN, int WN, int OCC, int BK>
+__global__ __launch_bounds__(128 * WN, OCC) void grouped_gemm_kernel(const GemmArgs g) {
+  constexpr bool RAGGED_K = (MODE == M_WG || MODE == M_WG1);
+  // the operand stages of the K loop (reused by the dA epilogue for H and dH)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<BM, BN, BK>()];
+  __shared__ float s_w[RAGGED_K ? 1 : BM];
+  __shared__ int s_slot[RAGGED_K ? 1 : BM];
+  __shared__ float s_part[MODE == M_DACT ? WN * BM : 1];
+  TileCoord tc;
+  if (!tile_coord<MODE, BM, BN>(g, tc)) return;
+  gemm_tile<MODE, BM, BN, WN, BK>(g, tc, smem, s_w, s_slot, s_part);
+}
+
+// ---------------------------------------------------------------------- single-launch forward
+// The forward's gather, up product with its scaled-SwiGLU epilogue and down product in one
+// persistent launch with a device work queue (the one-kernel MoE forward of the Mega MoE
+// announcement, section "Mega MoE คืออะไร?", here without the communication it overlaps).
+//
+// A work item is one row tile: 256 sorted rows of one expert.  Its block runs the up product
+// over all f/128 column tiles (H and As written as in the two-launch forward), waits for its own
+// stores, and then the down product over all of d for the same rows, reading As back through
+// its compute unit's path to L2.  No block ever waits for another: the only shared state is one
+// counter per queue, advanced by an atomic add per take.
+//
+// Queue layout (fwd_queue_kernel): expert e's row tiles go to queue e % 8, full tiles first in
+// expert order, then the partial last tiles, most rows first.  Block b drains queue b % 8 first
+// (the hardware deals blocks to the 8 XCDs round-robin, so that is one XCD's queue and the
+// tiles of one expert share its weights in that XCD's L2), then the other queues in turn.
+constexpr int kFqTotal = 0, kFqBeg = 16, kFqCnt = 32;  // qinfo words: total, 9 queue starts, 8 counters
+
+__global__ __launch_bounds__(1024) void fwd_queue_kernel(const int32_t* __restrict__ offsets, int E,
+                                                         int2* __restrict__ items, int32_t* __restrict__ qinfo) {
+  constexpr int BM = 256;
+  __shared__ int s_full[1024], s_rem[1024];
+  __shared__ int s_qbeg[9], s_qfull[8];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int full = c / BM, rem = c % BM;
+  s_full[e] = full;
+  s_rem[e] = rem;
+  __syncthreads();
+  if (e < 8) {
+    int nf = 0, np = 0;
+    for (int j = e; j < E; j += 8) {
+      nf += s_full[j];
+      np += s_rem[j] > 0;
+    }
+    s_qfull[e] = nf;
+    s_qbeg[e + 1] = nf + np;
+  }
+  __syncthreads();
+  if (e == 0) {
+    s_qbeg[0] = 0;
+    for (int q = 1; q <= 8; ++q) s_qbeg[q] += s_qbeg[q - 1];
+  }
+  __syncthreads();
+  if (e < E) {
+    const int q = e % 8;
+    int pos = s_qbeg[q];
+    for (int j = q; j < e; j += 8) pos += s_full[j];
+    for (int r = 0; r < full; ++r) items[pos + r] = make_int2(e, r);
+    if (rem > 0) {
+      int rank = 0;
+      for (int j = q; j < E; j += 8) {
+        const int rj = s_rem[j];
+        rank += (rj > rem) || (rj == rem && j < e);
+      }
+      items[s_qbeg[q] + s_qfull[q] + rank] = make_int2(e, full);
+    }
+  }
+  if (e <= 8) qinfo[kFqBeg + e] = s_qbeg[e];
+  if (e < 8) qinfo[kFqCnt + e] = 0;
+  if (e == 0) qinfo[kFqTotal] = s_qbeg[8];
+}
+
+// gu: the up product's arguments, gd: the down product's; BND: the down product's tile width.
+template <int BND>
+__global__ __launch_bounds__(512, 1) void fused_forward_kernel(const GemmArgs gu, const GemmArgs gd,
+                                                               const int2* __restrict__ items,
+                                                               int32_t* __restrict__ qinfo) {
+  constexpr int BM = 256;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[tile_lds_bytes<BM, 256, 64>()];
+  __shared__ float s_w[BM];
+  __shared__ int s_slot[BM];
+  __shared__ int s_item;
+  const int q0 = blockIdx.x % 8;
+  int tries = 0;  // thread 0: queues found empty so far, in the order q0, q0 + 1, ...
+  for (;;) {
+    __syncthreads();  // every wave is past the previous item (LDS arena, s_item)
+    if (threadIdx.x == 0) {
+      int it = -1;
+      for (; tries < 8; ++tries) {
+        const int q = (q0 + tries) & 7;
+        const int beg = qinfo[kFqBeg + q], n = qinfo[kFqBeg + q + 1] - beg;
+        const int i = atomicAdd(&qinfo[kFqCnt + q], 1);
+        if (i < n) {
+          it = beg + i;
+          break;
+        }
+      }
+      s_item = it;
+    }
+    __syncthreads();
+    const int item = s_item;
+    if (item < 0) break;  // uniform: every queue is drained
+    const int2 te = items[item];
+    TileCoord tc;
+    tc.e = te.x;
+    tc.m0 = gu.offsets[te.x] + te.y * BM;
+    tc.mrows = min(BM, gu.offsets[te.x + 1] - tc.m0);
+    tc.kbeg = 0;
+    tc.kchunk = 0;
+    tc.pslot = -1;
+    tc.kend = gu.K;
+    for (int nt = 0; nt < gu.f / 128; ++nt) {
+      if (nt > 0) __syncthreads();  // the previous tile's waves are out of the arena
+      tc.nt = nt;
+      tc.n0 = nt * 128;
+      gemm_tile<M_UP, BM, 256, 4, 64>(gu, tc, smem, s_w, s_slot, nullptr);
+    }
+    // The down product reads the As rows this block just stored: all of them complete first.
+    vm_wait<0>();
+    tc.kend = gd.K;
+    for (int nt = 0; nt < gd.N / BND; ++nt) {
+      __syncthreads();
+      tc.nt = nt;
+      tc.n0 = nt * BND;
+      gemm_tile<M_DOWN, BM, BND, 4, 64>(gd, tc, smem, s_w, s_slot, nullptr);
     }
   }
 }
@@ -692,9 +847,10 @@ int max_row_tiles(int64_t A, int E, int bm) {
   return (int)t;
 }
 
-hipError_t launch_gemm_up(const MoeShape& s, const uint16_t* x, const uint16_t* W1, const float* topk_w,
-                          const int32_t* offsets, const int32_t* perm, const int2* tiles, const int32_t* ntiles,
-                          uint16_t* H, uint16_t* As, hipStream_t st) {
+namespace {
+GemmArgs up_args(const MoeShape& s, const uint16_t* x, const uint16_t* W1, const float* topk_w,
+                 const int32_t* offsets, const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* H,
+                 uint16_t* As) {
   GemmArgs g = base_args(s, offsets, perm, tiles, ntiles);
   g.A = x;
   g.lda = s.d;
@@ -708,15 +864,11 @@ hipError_t launch_gemm_up(const MoeShape& s, const uint16_t* x, const uint16_t* 
   g.ldc0 = 2 * (int64_t)s.f;
   g.C1 = As;
   g.ldc1 = s.f;
-  const int64_t A = (int64_t)s.T * s.k;
-  const int bn = 256;  // 128 gate + 128 up columns (f is a multiple of 128)
-  dim3 grid((unsigned)(max_row_tiles(A, s.E, kGemmBM) * (s.f / (bn / 2))));
-  return run<M_UP>(g, kGemmBM, bn, grid, st);
+  return g;
 }
 
-hipError_t launch_gemm_down(const MoeShape& s, const uint16_t* As, const uint16_t* W2, const int32_t* offsets,
-                            const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* Op,
-                            hipStream_t st) {
+GemmArgs down_args(const MoeShape& s, const uint16_t* As, const uint16_t* W2, const int32_t* offsets,
+                   const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* Op) {
   GemmArgs g = base_args(s, offsets, perm, tiles, ntiles);
   g.A = As;
   g.lda = s.f;
@@ -727,10 +879,51 @@ hipError_t launch_gemm_down(const MoeShape& s, const uint16_t* As, const uint16_
   g.K = s.f;
   g.C0 = Op;
   g.ldc0 = s.d;
+  return g;
+}
+}  // namespace
+
+hipError_t launch_gemm_up(const MoeShape& s, const uint16_t* x, const uint16_t* W1, const float* topk_w,
+                          const int32_t* offsets, const int32_t* perm, const int2* tiles, const int32_t* ntiles,
+                          uint16_t* H, uint16_t* As, hipStream_t st) {
+  const GemmArgs g = up_args(s, x, W1, topk_w, offsets, perm, tiles, ntiles, H, As);
+  const int64_t A = (int64_t)s.T * s.k;
+  const int bn = 256;  // 128 gate + 128 up columns (f is a multiple of 128)
+  dim3 grid((unsigned)(max_row_tiles(A, s.E, kGemmBM) * (s.f / (bn / 2))));
+  return run<M_UP>(g, kGemmBM, bn, grid, st);
+}
+
+hipError_t launch_gemm_down(const MoeShape& s, const uint16_t* As, const uint16_t* W2, const int32_t* offsets,
+                            const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* Op,
+                            hipStream_t st) {
+  const GemmArgs g = down_args(s, As, W2, offsets, perm, tiles, ntiles, Op);
   const int64_t A = (int64_t)s.T * s.k;
   const int bn = pick_bn(s.d);
   dim3 grid((unsigned)(max_row_tiles(A, s.E, kGemmBM) * (s.d / bn)));
   return run<M_DOWN>(g, kGemmBM, bn, grid, st);
+}
+
+hipError_t launch_fwd_queue(const MoeShape& s, const int32_t* offsets, int2* items, int32_t* qinfo, hipStream_t st) {
+  fwd_queue_kernel<<<1, 1024, 0, st>>>(offsets, s.E, items, qinfo);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_forward(const MoeShape& s, const uint16_t* x, const uint16_t* W1, const uint16_t* W2,
+                                const float* topk_w, const int32_t* offsets, const int32_t* perm, const int2* items,
+                                int32_t* qinfo, uint16_t* H, uint16_t* As, uint16_t* Op, hipStream_t st) {
+  int dev = 0, ncu = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  if (ncu < 1) return hipErrorInvalidValue;
+  // one block per compute unit; the tile tables are not used (the queue replaces them)
+  const GemmArgs gu = up_args(s, x, W1, topk_w, offsets, perm, nullptr, nullptr, H, As);
+  const GemmArgs gd = down_args(s, As, W2, offsets, perm, nullptr, nullptr, Op);
+  if (s.d % 256 == 0)
+    fused_forward_kernel<256><<<ncu, 512, 0, st>>>(gu, gd, items, qinfo);
+  else
+    fused_forward_kernel<128><<<ncu, 512, 0, st>>>(gu, gd, items, qinfo);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_dact(const MoeShape& s, const uint16_t* dy, const uint16_t* W2, const uint16_t* H,

@@ -35,6 +35,12 @@ hipError_t launch_gemm_up(const MoeShape& s, const uint16_t* x, const uint16_t* 
 hipError_t launch_gemm_down(const MoeShape& s, const uint16_t* As, const uint16_t* W2, const int32_t* offsets,
                             const int32_t* perm, const int2* tiles, const int32_t* ntiles, uint16_t* Op,
                             hipStream_t st);
+// Single-launch forward: the work queue of row tiles (items: up to max_row_tiles(A, E, 256)
+// entries; qinfo: 40 words), then GEMM1 and GEMM2 of every row tile in one persistent launch.
+hipError_t launch_fwd_queue(const MoeShape& s, const int32_t* offsets, int2* items, int32_t* qinfo, hipStream_t st);
+hipError_t launch_fused_forward(const MoeShape& s, const uint16_t* x, const uint16_t* W1, const uint16_t* W2,
+                                const float* topk_w, const int32_t* offsets, const int32_t* perm, const int2* items,
+                                int32_t* qinfo, uint16_t* H, uint16_t* As, uint16_t* Op, hipStream_t st);
 // dA: G = dy[perm/k] . W2[e]^T; epilogue -> dH (dSwiGLU) and d_topk_w partials.
 hipError_t launch_gemm_dact(const MoeShape& s, const uint16_t* dy, const uint16_t* W2, const uint16_t* H,
                             const float* topk_w, const int32_t* offsets, const int32_t* perm, const int2* tiles,

@@ -145,6 +145,22 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale,
                 const int32_t* inv_perm, void* y, void* saved, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* The bf16 moe_forward with the dispatch gather, both grouped GEMMs and the scaled SwiGLU in one
+ * persistent launch fed by a device work queue, followed by the combine ([Mega] "Mega MoE
+ * คืออะไร?" [what is Mega MoE?]: dispatch, the two linear layers and SwiGLU fused into one
+ * kernel).  Same arguments, results and `saved` contents as moe_forward with dtype MOE_BF16 and
+ * NULL scales, so moe_backward accepts its `saved`; y, H and As are bitwise equal to
+ * moe_forward's.  A work item is a row tile (256 sorted rows of one expert): its block runs the
+ * up product over all of f, then the down product over all of d for the same rows, so the work
+ * is coarser than moe_forward's per-tile launches (slower when the row tiles are few against the
+ * compute units).  Blocks take items with atomic adds on counters in `ws` and never wait for
+ * one another; `ws` needs moe_workspace_bytes(MOE_WS_FORWARD).  dtype other than MOE_BF16:
+ * MOE_ERR_DTYPE.  Other errors as moe_forward. */
+int moe_forward_fused(const moe_dims* dims, const void* x, const void* W1, const void* W2,
+                      const float* topk_w, const int32_t* offsets, const int32_t* perm,
+                      const int32_t* inv_perm, void* y, void* saved, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Backward of moe_forward for L = sum(dy * y) ([Prime] "Mit csinált a Prime Intellect?" [what
  * did Prime Intellect do?]: a backward pass for the fused MoE kernel).  Writes dx (bf16),
  * dW1 and dW2 (bf16; an expert with no routed pair gets exactly zero), d_topk_w (fp32, 0 on

@@ -153,6 +153,25 @@ def test_forward_backward_argument_errors(lib):
     assert lib.moe_forward(ctypes.byref(empty), *([None] * 13), 0, None) == moe.MOE_OK
 
 
+def test_fused_forward_argument_errors(lib):
+    dm = moe.dims(64, 128, 256, 8, 2)
+    _, wf = sz(lib, dm, moe.MOE_WS_FORWARD)
+    F = FAKE
+    fused = lambda **o: lib.moe_forward_fused(ctypes.byref(o.get("dm", dm)), o.get("x", F), F, F, F, F, F, F,
+                                              o.get("y", F), o.get("saved", F), F, o.get("ws", wf), None)
+    assert fused(x=None) == moe.MOE_ERR_NULL
+    assert fused(y=None) == moe.MOE_ERR_NULL
+    assert fused(saved=None) == moe.MOE_ERR_NULL
+    assert fused(ws=wf - 1) == moe.MOE_ERR_WORKSPACE
+    assert fused(x=F + 2) == moe.MOE_ERR_ALIGN
+    assert fused(saved=F + 16) == moe.MOE_ERR_ALIGN
+    assert fused(dm=moe.dims(64, 128, 200, 8, 2)) == moe.MOE_ERR_SHAPE
+    for dt in (moe.MOE_FP8_E4M3, moe.MOE_MXFP8):           # bf16 only
+        assert fused(dm=moe.dims(64, 256, 256, 8, 2, dtype=dt)) == moe.MOE_ERR_DTYPE
+    empty = moe.dims(0, 128, 256, 8, 2)
+    assert lib.moe_forward_fused(ctypes.byref(empty), *([None] * 10), 0, None) == moe.MOE_OK
+
+
 def test_mxfp8_argument_rules(lib):
     F = FAKE
     mx = moe.dims(64, 256, 256, 8, 2, dtype=moe.MOE_MXFP8)
