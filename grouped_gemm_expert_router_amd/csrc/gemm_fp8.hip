@@ -197,7 +197,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
 
   // One K stage = one 128-wide scale block: per 32-row fragment i, two 64-deep MFMAs per B
   // fragment into a temporary, then acc += temp * s_a(row) * s_b(block).  Row-fragment-major
-  // order keeps only FN temporaries live next to the accumulators.
+  // order keeps only FN temporaries live next to the accumulators.  The MFMAs take the B
+  // fragment as their first operand, so each 32x32 block is held transposed: lane l holds row
+  // l % 32 of the fragment (one row scale per lane) and 16 of its columns, all in one 128-column
+  // weight block, so a block's promotion is one scale product and 16 fmas per lane.
   // In an expert's last row tile, a wave whose rows all lie past the expert's end skips its
   // fragment reads and MFMAs (uniform: mrows and wm are); it still issues its DMA share.
   const bool busy = __builtin_amdgcn_readfirstlane(wm * TM < mrows);
@@ -217,6 +220,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
       const int nb = b_block(j);
       sb[j] = B_KN ? Bs[(int64_t)kb * g.bs_ld + nb] : Bs[(int64_t)nb * g.bs_ld + kb];
     }
+    // the scale of the lane's row in each row fragment (rows 32w.. of the stage sit at 256 * w)
+    float sa[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      sa[i] = *(const LDS_AS float*)(uintptr_t)(sbase + (wm * FM + i) * 256 + (lane & 31) * 4);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int arow = wm * TM + i * 32 + (lane & 31);
@@ -227,33 +235,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const f32x16_t z = {};
-          t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bv[kk][j], kk == 0 ? z : t[j], 0, 0, 0, 127, 0,
+          t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[kk][j], af, kk == 0 ? z : t[j], 0, 0, 0, 127, 0,
                                                                  127);
         }
       }
-      float sa[16];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = wm * TM + i * 32 + 8 * rr + 4 * (lane >> 5);  // 4 consecutive rows
-        const f32x4_t v = *(const LDS_AS f32x4_t*)(uintptr_t)(sbase + (row >> 5) * 256 + (row & 31) * 4);
-        sa[4 * rr] = v[0];
-        sa[4 * rr + 1] = v[1];
-        sa[4 * rr + 2] = v[2];
-        sa[4 * rr + 3] = v[3];
-      }
-      if constexpr (MODE == F_UP) {
+      for (int j = 0; j < FN; ++j) {
+        const float s2 = sa[i] * sb[j];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[j][r], sa[r] * sb[j], acc[i][j][r]);
-      } else {
-        // the wave's FN fragments lie in one 128-column block: one s_b
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s2 = sa[r] * sb[0];
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j][r] = fmaf(t[j][r], s2, acc[i][j][r]);
-        }
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[j][r], s2, acc[i][j][r]);
       }
     }
   };
@@ -276,11 +266,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int c = b_row(j) + lcol;
+      // transposed block: lane l holds band row 32*wm + l%32, columns 8*(r/4) + 4*(l/32) + r%4
+      const int q = 32 * wm + lcol;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        cband[q * CPAD + c] = acc[i][j][r];
+      for (int r = 0; r < 16; r += 4) {
+        const int c = b_row(j) + 8 * (r >> 2) + 4 * (lane >> 5);
+        *(float4*)&cband[q * CPAD + c] = make_float4(acc[i][j][r], acc[i][j][r + 1], acc[i][j][r + 2], acc[i][j][r + 3]);
       }
     }
     __syncthreads();
