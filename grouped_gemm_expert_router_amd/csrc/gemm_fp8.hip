@@ -196,8 +196,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // One K stage = one 128-wide scale block: per 32-row fragment i, two 64-deep MFMAs per B
-  // fragment into a temporary, then acc += temp * s_a(row) * s_b(block).  Row-fragment-major
-  // order keeps only FN temporaries live next to the accumulators.  The MFMAs take the B
+  // fragment into a temporary, then acc += temp * s_a(row) * s_b(block).  The MFMAs take the B
   // fragment as their first operand, so each 32x32 block is held transposed: lane l holds row
   // l % 32 of the fragment (one row scale per lane) and 16 of its columns, all in one 128-column
   // weight block, so a block's promotion is one scale product and 16 fmas per lane.
@@ -225,25 +224,49 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       sa[i] = *(const LDS_AS float*)(uintptr_t)(sbase + (wm * FM + i) * 256 + (lane & 31) * 4);
+    // Software pipeline over the row fragments, in a fixed order (scheduling fences): the
+    // promotion of block (i, 0) runs under the MFMA of (i, 1) and that of (i, 1) under the first
+    // MFMA of (i + 1, 0), each temporary being rewritten only after its promotion has read it;
+    // the next row fragment's k halves are read from LDS as soon as the current ones have been
+    // consumed.  Same registers as a plain loop: two temporaries, two A fragments.
+    static_assert(FN == 2, "pipeline written for two column fragments per wave");
+    auto mfma = [&](const i32x8& b, const i32x8& a, const f32x16_t& c) __attribute__((always_inline)) {
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
+    };
+    auto promote = [&](int i, int j, const f32x16_t& t) __attribute__((always_inline)) {
+      const float s2 = sa[i] * sb[j];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[r], s2, acc[i][j][r]);
+    };
+    auto arow = [&](int i) __attribute__((always_inline)) { return wm * TM + i * 32 + (lane & 31); };
+    const f32x16_t z = {};
+    i32x8 a0 = read_km8(abase, arow(0), 0, lane), a1 = read_km8(abase, arow(0), 1, lane);
+    f32x16_t t0 = mfma(bv[0][0], a0, z), t1 = mfma(bv[0][1], a0, z);
+    __builtin_amdgcn_sched_barrier(0);
+    if (FM > 1) a0 = read_km8(abase, arow(1), 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    t0 = mfma(bv[1][0], a1, t0);
+    t1 = mfma(bv[1][1], a1, t1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (FM > 1) a1 = read_km8(abase, arow(1), 1, lane);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int arow = wm * TM + i * 32 + (lane & 31);
-      f32x16_t t[FN];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const i32x8 af = read_km8(abase, arow, kk, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const f32x16_t z = {};
-          t[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[kk][j], af, kk == 0 ? z : t[j], 0, 0, 0, 127, 0,
-                                                                 127);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const float s2 = sa[i] * sb[j];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[j][r], s2, acc[i][j][r]);
+      __builtin_amdgcn_sched_barrier(0);
+      promote(i, 0, t0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < FM) t0 = mfma(bv[0][0], a0, z);
+      __builtin_amdgcn_sched_barrier(0);
+      promote(i, 1, t1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < FM) {
+        t1 = mfma(bv[0][1], a0, z);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 2 < FM) a0 = read_km8(abase, arow(i + 2), 0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        t0 = mfma(bv[1][0], a1, t0);
+        t1 = mfma(bv[1][1], a1, t1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 2 < FM) a1 = read_km8(abase, arow(i + 2), 1, lane);
       }
     }
   };
