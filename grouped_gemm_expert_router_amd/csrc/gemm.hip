@@ -468,24 +468,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const TileCoord& tc
   // four 4-column groups of lanes l and l+32 into two runs of 8 consecutive columns each, at
   // 8h and 16 + 8h (h = l/32), which are stored as 16-byte chunks straight from registers.
   const int h = lane >> 5, lrow = lane & 31;
-  // bf16 of one block in that order: lo = columns 8h..8h+7, hi = columns 16+8h..23+8h
   auto pack_rows = [&](const f32x16_t& v, uint4& lo, uint4& hi) __attribute__((always_inline)) {
-    uint32_t p[4][2];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      p[q][0] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
-      p[q][1] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; a += 2)
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const auto r = __builtin_amdgcn_permlane32_swap(p[a][d], p[a + 1][d], false, false);
-        p[a][d] = r[0];
-        p[a + 1][d] = r[1];
-      }
-    lo = make_uint4(p[0][0], p[0][1], p[1][0], p[1][1]);
-    hi = make_uint4(p[2][0], p[2][1], p[3][0], p[3][1]);
+    pack_rows_bf16(v, lo, hi);
   };
 
   if constexpr (MODE == M_UP) {

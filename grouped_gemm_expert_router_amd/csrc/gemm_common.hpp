@@ -197,6 +197,29 @@ __device__ __forceinline__ i32x8 read_km8_mx(uint32_t base, int row, int kk, int
   return v;
 }
 
+// A transposed 32x32 accumulator block (lane l holds row l % 32; element r is column
+// 8*(r/4) + 4*(l/32) + r%4) as bf16 runs of 8 consecutive columns: v_permlane32_swap trades
+// halves between lanes l and l+32, leaving lo = columns 8h..8h+7 and hi = columns 16+8h..23+8h
+// (h = l/32), each one 16-byte store.
+__device__ __forceinline__ void pack_rows_bf16(const f32x16_t& v, uint4& lo, uint4& hi) {
+  uint32_t p[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    p[q][0] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
+    p[q][1] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; a += 2)
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const auto r = __builtin_amdgcn_permlane32_swap(p[a][d], p[a + 1][d], false, false);
+      p[a][d] = r[0];
+      p[a + 1][d] = r[1];
+    }
+  lo = make_uint4(p[0][0], p[0][1], p[1][0], p[1][1]);
+  hi = make_uint4(p[2][0], p[2][1], p[3][0], p[3][1]);
+}
+
 // e4m3 with round to nearest even, saturating at +-448.
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
   auto sat = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };

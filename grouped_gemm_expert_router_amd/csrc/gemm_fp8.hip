@@ -285,8 +285,25 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   // ------------------------------------------------------------------ epilogues (LDS band)
   const int lcol = lane & 31;
   constexpr int CH = BN / 8;
+  // DACT: 32 threads per row, 8 columns each, ITEMS rows per thread and phase
+  constexpr int ITEMS = 64 * CH / NTH;
+  static_assert(MODE != F_DACT || ITEMS * NTH == 64 * CH, "dA band items");
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    auto tile_row = [&](int q) __attribute__((always_inline)) { return (q >> 5) * TM + 32 * i + (q & 31); };
+    // DACT: the phase's H loads go out before the band is written, so their latency hides
+    // behind the band writes and the barrier
+    uint4 hgv[ITEMS], huv[ITEMS];
+    if constexpr (MODE == F_DACT) {
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int id = tid + it * NTH, q = id / CH, cc = id % CH;
+        const int lr = tile_row(q);
+        const int64_t pos = m0 + (lr < mrows ? lr : 0);  // rows past the expert's end read row m0
+        hgv[it] = *(const uint4*)&g.Hs[pos * g.ldh + n0 + cc * 8];
+        huv[it] = *(const uint4*)&g.Hs[pos * g.ldh + g.f + n0 + cc * 8];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       // transposed block: lane l holds band row 32*wm + l%32, columns 8*(r/4) + 4*(l/32) + r%4
@@ -298,7 +315,6 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
       }
     }
     __syncthreads();
-    auto tile_row = [&](int q) __attribute__((always_inline)) { return (q >> 5) * TM + 32 * i + (q & 31); };
     if constexpr (MODE == F_UP) {
       // 16 lanes per row: 8 gate + 8 up columns each; As's 128 columns of the tile form one block
       for (int id = tid; id < 64 * (CH / 2); id += NTH) {
@@ -333,20 +349,19 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
       }
     } else if constexpr (MODE == F_DACT) {
       // 32 lanes per row (8 columns each): dSwiGLU, routing-weight partial, dH in bf16 and e4m3
-      for (int id = tid; id < 64 * CH; id += NTH) {
-        const int q = id / CH, cc = id % CH;
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int id = tid + it * NTH, q = id / CH, cc = id % CH;
         const int lr = tile_row(q);
         const bool ok = lr < mrows;
         const int64_t pos = m0 + (ok ? lr : 0);
         const int col = n0 + cc * 8;
-        const uint4 hgv = *(const uint4*)&g.Hs[pos * g.ldh + col];
-        const uint4 huv = *(const uint4*)&g.Hs[pos * g.ldh + g.f + col];
         const float* Gp = &cband[q * CPAD + cc * 8];
         const float w = s_w[lr];
         float part = 0.0f, dg[8], du[8];
 #pragma unroll
         for (int t2 = 0; t2 < 4; ++t2) {
-          const uint32_t wg = word_of(hgv, t2), wu = word_of(huv, t2);
+          const uint32_t wg = word_of(hgv[it], t2), wu = word_of(huv[it], t2);
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const float gv = hh ? hi_bf16(wg) : lo_bf16(wg), uv = hh ? hi_bf16(wu) : lo_bf16(wu);
