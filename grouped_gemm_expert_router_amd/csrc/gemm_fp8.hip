@@ -123,7 +123,6 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
     s_w[r] = wv;
   }
   const uint8_t* Bexp = g.B + (int64_t)e * g.b_estride;
-  const CONST_AS float* Bs = (const CONST_AS float*)g.B_scale + (int64_t)e * g.bs_estride;
 
   // ------------------------------------------------------------------ DMA sources
   // A (KM, 256 rows x 128 bytes): block gi = 4*wave + q holds rows 8*gi..8*gi+7.
@@ -136,13 +135,26 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
     const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
     a_src[q] = g.A + src * g.lda + 16 * c;
   }
-  // A row scales: wave w brings rows 32w..32w+31 (lanes past 31 repeat row 32w + 31).
+  // Scales of a K stage, one 4-byte DMA per wave into its 256-byte slot: lanes 0..31 bring the
+  // row scales of rows 32w..32w+31, lanes 32 and 33 the weight-block scales of the wave's two
+  // B fragments (lanes past 33 repeat lane 32).  Each lane's source advances by sc_step floats
+  // per stage.  With no scalar load in the K loop the stage's LDS reads retire in order, so each
+  // MFMA waits only for its own fragments.
   const float* sc_src;
-  {
-    const int row = 32 * wave + min(lane, 31);
+  int sc_step;
+  if (lane < 32) {
+    const int row = 32 * wave + lane;
     const int pos = m0 + (row < mrows ? row : 0);
     const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
     sc_src = g.A_scale + src * g.lds_a;
+    sc_step = 1;
+  } else {
+    const int j = lane == 33 ? 1 : 0;
+    int nb;  // 128-column block of the weight matrix holding B fragment j
+    if constexpr (MODE == F_UP) nb = j == 0 ? nt : g.f / 128 + nt;  // gate / up columns of the tile
+    else nb = (n0 + wn * (BN / WN) + j * 32) / 128;
+    sc_src = g.B_scale + (int64_t)e * g.bs_estride + (B_KN ? (int64_t)nb : (int64_t)nb * g.bs_ld);
+    sc_step = B_KN ? g.bs_ld : 1;
   }
   const uint8_t* b_src[QB];
 #pragma unroll
@@ -169,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
 #pragma unroll
     for (int q = 0; q < QB; ++q)
       dma16(B_KN ? b_src[q] + (int64_t)k0 * g.ldb : b_src[q] + k0, bbase + (wave * QB + q) * 1024);
-    dma4(sc_src + t, sbase + wave * 256);
+    dma4(sc_src + (int64_t)t * sc_step, sbase + wave * 256);
   };
 
   // LDS column of the wave's j-th 32-column B fragment (UP: gate fragments, then up fragments)
@@ -178,13 +190,6 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
       return j < FN / 2 ? wn * (TN / 2) + j * 32 : BN / 2 + wn * (TN / 2) + (j - FN / 2) * 32;
     else
       return wn * TN + j * 32;
-  };
-  // 128-column block of the weight matrix holding B fragment j
-  auto b_block = [&](int j) __attribute__((always_inline)) -> int {
-    if constexpr (MODE == F_UP)
-      return j < FN / 2 ? nt : g.f / 128 + nt;  // BN/2 = 128: the gate (up) columns of a tile are one block
-    else
-      return (n0 + wn * TN + j * 32) / 128;
   };
 
   f32x16_t acc[FM][FN];
@@ -203,27 +208,32 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   // In an expert's last row tile, a wave whose rows all lie past the expert's end skips its
   // fragment reads and MFMAs (uniform: mrows and wm are); it still issues its DMA share.
   const bool busy = __builtin_amdgcn_readfirstlane(wm * TM < mrows);
-  auto compute = [&](int st, int kb) __attribute__((always_inline)) {
+  auto compute = [&](int st) __attribute__((always_inline)) {
     const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES, sbase = bbase + B_BYTES;
+    auto arow = [&](int i) __attribute__((always_inline)) { return wm * TM + i * 32 + (lane & 31); };
+    // LDS reads in the order of first use: the first k half's B fragments and A fragment, then
+    // the second half's, then the scales
     i32x8 bv[2][FN];
+    i32x8 a0, a1;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if constexpr (B_KN) bv[kk][j] = read_kn8(bbase, b_row(j), kk, lane);
         else bv[kk][j] = read_km8(bbase, b_row(j) + (lane & 31), kk, lane);
       }
-    float sb[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int nb = b_block(j);
-      sb[j] = B_KN ? Bs[(int64_t)kb * g.bs_ld + nb] : Bs[(int64_t)nb * g.bs_ld + kb];
+      if (kk == 0) a0 = read_km8(abase, arow(0), 0, lane);
+      else a1 = read_km8(abase, arow(0), 1, lane);
     }
     // the scale of the lane's row in each row fragment (rows 32w.. of the stage sit at 256 * w)
-    float sa[FM];
+    // and the wave's two weight-block scales (words 32, 33 of its own slot)
+    float sa[FM], sb[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       sa[i] = *(const LDS_AS float*)(uintptr_t)(sbase + (wm * FM + i) * 256 + (lane & 31) * 4);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sb[j] = *(const LDS_AS float*)(uintptr_t)(sbase + wave * 256 + (32 + j) * 4);
+    __builtin_amdgcn_sched_barrier(0);
     // Software pipeline over the row fragments, in a fixed order (scheduling fences): the
     // promotion of block (i, 0) runs under the MFMA of (i, 1) and that of (i, 1) under the first
     // MFMA of (i + 1, 0), each temporary being rewritten only after its promotion has read it;
@@ -238,9 +248,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(t[r], s2, acc[i][j][r]);
     };
-    auto arow = [&](int i) __attribute__((always_inline)) { return wm * TM + i * 32 + (lane & 31); };
     const f32x16_t z = {};
-    i32x8 a0 = read_km8(abase, arow(0), 0, lane), a1 = read_km8(abase, arow(0), 1, lane);
     f32x16_t t0 = mfma(bv[0][0], a0, z), t1 = mfma(bv[0][1], a0, z);
     __builtin_amdgcn_sched_barrier(0);
     if (FM > 1) a0 = read_km8(abase, arow(1), 0, lane);
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   for (int it = 0; it < nk; ++it) {
     vm_lgkm_wait_barrier<0>();
     if (it + 1 < nk) issue(it + 1, (it + 1) % S);
-    if (busy) compute(it % S, it);
+    if (busy) compute(it % S);
   }
   __syncthreads();
 
