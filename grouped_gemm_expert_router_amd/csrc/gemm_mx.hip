@@ -237,18 +237,35 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
         for (int kk = 0; kk < 2; ++kk) sbw[kk][j] = (dw >> (8 * (2 * kk + kbsel))) & 0xFFu;
       }
     }
+    // A fragments one (row fragment, k half) step ahead: the LDS read of step q + 1 is in
+    // flight while the MFMAs of step q run (reads retire in order, so each MFMA waits for its own
+    // fragment only)
+    auto arow = [&](int i) __attribute__((always_inline)) { return wm * TM + i * 32 + (lane & 31); };
+    auto a_exp = [&](int i) __attribute__((always_inline)) {
+      return *(const LDS_AS uint32_t*)(uintptr_t)(aebase + (arow(i) >> 5) * 256 + (arow(i) & 31) * 4);
+    };
+    i32x8 af = read_km8_mx(abase, arow(0), 0, lane);
+    uint32_t adw = a_exp(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int arow = wm * TM + i * 32 + (lane & 31);
-      const uint32_t adw = *(const LDS_AS uint32_t*)(uintptr_t)(aebase + (arow >> 5) * 256 + (arow & 31) * 4);
+    for (int q = 0; q < 2 * FM; ++q) {
+      const int i = q >> 1, kk = q & 1;
+      i32x8 af_next;
+      uint32_t adw_next = adw;
+      if (q + 1 < 2 * FM) {
+        af_next = read_km8_mx(abase, arow((q + 1) >> 1), (q + 1) & 1, lane);
+        if (kk == 1) adw_next = a_exp(i + 1);
+      }
+      const int sa = (int)((adw >> (8 * (2 * kk + kbsel))) & 0xFFu);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const i32x8 af = read_km8_mx(abase, arow, kk, lane);
-        const int sa = (int)((adw >> (8 * (2 * kk + kbsel))) & 0xFFu);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bv[kk][j], acc[i][j], 0, 0, 0, sa, 0,
-                                                                      (int)sbw[kk][j]);
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bv[kk][j], acc[i][j], 0, 0, 0, sa, 0,
+                                                                    (int)sbw[kk][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q + 1 < 2 * FM) {
+        af = af_next;
+        adw = adw_next;
       }
     }
   };
@@ -953,17 +970,32 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_wg_kernel(const MxWgAr
         bv[kk][j] = read_kn8_mx(bbase, col, kk, lane);
         sb[kk][j] = *(const LDS_AS uint8_t*)(uintptr_t)(bebase + (2 * kk + kbsel) * 256 + col + (lane & 31));
       }
+    // A fragments and their exponents one (row fragment, k half) step ahead, as in the
+    // ragged-M kernel
+    auto a_frag = [&](int q, i32x8& af, int& sa) __attribute__((always_inline)) {
+      const int row = wm * TM + 32 * (q >> 1), kk = q & 1;
+      af = read_kn8_mx(abase, row, kk, lane);
+      sa = *(const LDS_AS uint8_t*)(uintptr_t)(aebase + (2 * kk + kbsel) * 256 + row + (lane & 31));
+    };
+    i32x8 af;
+    int sa;
+    a_frag(0, af, sa);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wm * TM + 32 * i;
+    for (int q = 0; q < 2 * FM; ++q) {
+      const int i = q >> 1, kk = q & 1;
+      i32x8 af_next;
+      int sa_next = 0;
+      if (q + 1 < 2 * FM) a_frag(q + 1, af_next, sa_next);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const i32x8 af = read_kn8_mx(abase, row, kk, lane);
-        const int sa = *(const LDS_AS uint8_t*)(uintptr_t)(aebase + (2 * kk + kbsel) * 256 + row + (lane & 31));
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[kk][j], af, acc[i][j], 0, 0, 0, sb[kk][j], 0,
-                                                                      sa);
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv[kk][j], af, acc[i][j], 0, 0, 0, sb[kk][j], 0,
+                                                                    sa);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q + 1 < 2 * FM) {
+        af = af_next;
+        sa = sa_next;
       }
     }
   };
