@@ -87,7 +87,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   constexpr int QA = A_BYTES / (1024 * NW), QB = B_BYTES / (1024 * NW);
   constexpr int CPAD = BN + 4;
-  constexpr int CBAND_BYTES = 2 * 32 * CPAD * 4;
+  constexpr int PH = 2;  // row fragments per epilogue phase: the band holds 64 * PH rows
+  constexpr int CBAND_BYTES = 2 * 32 * PH * CPAD * 4;
   constexpr int ARENA = S * STAGE > CBAND_BYTES ? S * STAGE : CBAND_BYTES;
   static_assert(BM == 256 && QA == 4 && QB == 4, "DMA split");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[ARENA];
@@ -294,11 +295,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
   const int lcol = lane & 31;
   constexpr int CH = BN / 8;
   // DACT: 32 threads per row, 8 columns each, ITEMS rows per thread and phase
-  constexpr int ITEMS = 64 * CH / NTH;
-  static_assert(MODE != F_DACT || ITEMS * NTH == 64 * CH, "dA band items");
+  constexpr int BR = 64 * PH, ITEMS = BR * CH / NTH;  // band rows, dA items per thread
+  static_assert(FM % PH == 0 && (MODE != F_DACT || ITEMS * NTH == BR * CH), "epilogue band");
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    auto tile_row = [&](int q) __attribute__((always_inline)) { return (q >> 5) * TM + 32 * i + (q & 31); };
+  for (int ph = 0; ph < FM / PH; ++ph) {
+    // band row q: wave row q / (32*PH), row fragment PH*ph + (q % (32*PH)) / 32, row q % 32
+    auto tile_row = [&](int q) __attribute__((always_inline)) {
+      return (q / (32 * PH)) * TM + 32 * (PH * ph + (q % (32 * PH)) / 32) + (q & 31);
+    };
     // DACT: the phase's H loads go out before the band is written, so their latency hides
     // behind the band writes and the barrier
     uint4 hgv[ITEMS], huv[ITEMS];
@@ -313,19 +317,22 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
       }
     }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      // transposed block: lane l holds band row 32*wm + l%32, columns 8*(r/4) + 4*(l/32) + r%4
-      const int q = 32 * wm + lcol;
+    for (int ii = 0; ii < PH; ++ii)
 #pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        const int c = b_row(j) + 8 * (r >> 2) + 4 * (lane >> 5);
-        *(float4*)&cband[q * CPAD + c] = make_float4(acc[i][j][r], acc[i][j][r + 1], acc[i][j][r + 2], acc[i][j][r + 3]);
+      for (int j = 0; j < FN; ++j) {
+        // transposed block: lane l holds band row 32*PH*wm + 32*ii + l%32, columns
+        // 8*(r/4) + 4*(l/32) + r%4
+        const int i = PH * ph + ii, q = 32 * PH * wm + 32 * ii + lcol;
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const int c = b_row(j) + 8 * (r >> 2) + 4 * (lane >> 5);
+          *(float4*)&cband[q * CPAD + c] = make_float4(acc[i][j][r], acc[i][j][r + 1], acc[i][j][r + 2], acc[i][j][r + 3]);
+        }
       }
-    }
     __syncthreads();
     if constexpr (MODE == F_UP) {
       // 16 lanes per row: 8 gate + 8 up columns each; As's 128 columns of the tile form one block
-      for (int id = tid; id < 64 * (CH / 2); id += NTH) {
+      for (int id = tid; id < BR * (CH / 2); id += NTH) {
         const int q = id / (CH / 2), cc = id % (CH / 2);
         const int lr = tile_row(q);
         const bool ok = lr < mrows;
@@ -400,7 +407,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
         }
       }
     } else {
-      for (int id = tid; id < 64 * CH; id += NTH) {
+      for (int id = tid; id < BR * CH; id += NTH) {
         const int q = id / CH, cc = id % CH;
         const int lr = tile_row(q);
         if (lr < mrows) {
