@@ -361,7 +361,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const TileCoord& tc
     const uint32_t abase = lds0 + st * STAGE, bbase = abase + A_BYTES;
     constexpr int KS = BK / 16;
     bf16x8_t af[2][FM], bv[2][FN];
-    load_frags(abase, bbase, 0, af[0], bv[0]);
+    // first k step: the first MFMA's operands (A fragment 0, B fragment 0) are read first, so
+    // the MFMAs can start before the whole step's fragments have arrived
+    auto read_a = [&](int i, int kk) __attribute__((always_inline)) {
+      if constexpr (A_KN) return read_kn<BM>(abase, wm * TM + i * 32, kk, lane);
+      else return read_km<BK>(abase, wm * TM + i * 32 + (lane & 31), 2 * kk + (lane >> 5));
+    };
+    auto read_b = [&](int j, int kk) __attribute__((always_inline)) {
+      if constexpr (B_KN) return read_kn<BN>(bbase, b_row(j), kk, lane);
+      else return read_km<BK>(bbase, b_row(j) + (lane & 31), 2 * kk + (lane >> 5));
+    };
+    af[0][0] = read_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      bv[0][j] = read_b(j, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 1; i < FM; ++i) {
+      af[0][i] = read_a(i, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // Raised wave priority while the MFMAs issue: with two waves per SIMD, the arbiter then
     // favours the wave that feeds the matrix pipe over one issuing its DMA.
     __builtin_amdgcn_s_setprio(1);
@@ -458,6 +479,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const TileCoord& tc
     // does not read, under that step's MFMAs
     if constexpr (MODE == M_DACT)
       if (it == nk - 1 && busy) dact_h_dma(0, (it + 1) % S);
+    // Ragged K: the token scalar load may still be outstanding here on the path without a
+    // refill; retiring it now (visibly to the compiler's wait-count tracking) lets the step's
+    // first MFMAs wait for their own LDS reads only instead of for every outstanding one.
+    if constexpr (RAGGED_K) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     if (busy) compute(it % S);
   }
 
