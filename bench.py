@@ -458,6 +458,28 @@ def main():
     ms = start.elapsed_time(stop) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step")
 
+    # The same K steps replayed from a HIP graph captured once (every entry point only enqueues
+    # kernels on the caller's stream): the step without host launch overhead.
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        step()
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    start.record(cur)
+    for _ in range(args.steps):
+        graph.replay()
+    stop.record(cur)
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(stop) / args.steps
+    del graph
+    log(f"[bench] timed {args.steps} graph replays: {ms_graph:.3f} ms/step")
+
     events, open_ev, streams = [], {}, {}
 
     def hook(stage, begin, stream_ptr):
@@ -640,7 +662,8 @@ def main():
         "tokens_per_s": T / (ms * 1e-3),
         "frac_of_bf16_peak": tflops / PEAK_TFLOPS["bf16"],
         "frac_of_mfma_peak": ideal_ms / ms,
-        "useful_flop_per_step": useful, "ms_per_step_with_stage_events": ms_ev, "stages": stages,
+        "useful_flop_per_step": useful, "ms_per_step_with_stage_events": ms_ev,
+        "ms_per_step_graph_replay": ms_graph, "stages": stages,
         "permute_standalone": permute, "router_front_end": router, "single_launch_forward": fused,
         "roofline": roof,
         "llc_cold": cold, "cpu_baseline": cpu,
