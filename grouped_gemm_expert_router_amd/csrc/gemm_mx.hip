@@ -94,7 +94,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
   constexpr int STAGE = A_BYTES + B_BYTES + AE_BYTES + BE_BYTES;
   constexpr int QA = A_BYTES / (1024 * NW), QB = B_BYTES / (1024 * NW);
   constexpr int CPAD = BN + 4;
-  constexpr int CBAND_BYTES = 2 * 32 * CPAD * 4;
+  constexpr int PH = 2;  // row fragments per epilogue phase: the band holds 64 * PH rows
+  constexpr int CBAND_BYTES = 2 * 32 * PH * CPAD * 4;
   constexpr int ARENA = S * STAGE > CBAND_BYTES ? S * STAGE : CBAND_BYTES;
   static_assert(BM == 256 && QA == 4 && QB == 4, "DMA split");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[ARENA];
@@ -287,22 +288,43 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
   // ------------------------------------------------------------------ epilogues (LDS band)
   const int lcol = lane & 31;
   constexpr int CH = BN / 8;
+  // DACT: 32 threads per row, 8 columns each, ITEMS rows per thread and phase
+  constexpr int BR = 64 * PH, ITEMS = BR * CH / NTH;  // band rows, dA items per thread
+  static_assert(FM % PH == 0 && (MODE != X_DACT || ITEMS * NTH == BR * CH), "epilogue band");
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int ph = 0; ph < FM / PH; ++ph) {
+    // band row q: wave row q / (32*PH), row fragment PH*ph + (q % (32*PH)) / 32, row q % 32
+    auto tile_row = [&](int q) __attribute__((always_inline)) {
+      return (q / (32 * PH)) * TM + 32 * (PH * ph + (q % (32 * PH)) / 32) + (q & 31);
+    };
+    // DACT: the phase's H loads go out before the band is written, so their latency hides
+    // behind the band writes and the barrier
+    uint4 hgv[ITEMS], huv[ITEMS];
+    if constexpr (MODE == X_DACT) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int c = b_row(j) + lcol;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        cband[q * CPAD + c] = acc[i][j][r];
+      for (int it = 0; it < ITEMS; ++it) {
+        const int id = tid + it * NTH, q = id / CH, cc = id % CH;
+        const int lr = tile_row(q);
+        const int64_t pos = m0 + (lr < mrows ? lr : 0);  // rows past the expert's end read row m0
+        hgv[it] = *(const uint4*)&g.Hs[pos * g.ldh + n0 + cc * 8];
+        huv[it] = *(const uint4*)&g.Hs[pos * g.ldh + g.f + n0 + cc * 8];
       }
     }
+#pragma unroll
+    for (int ii = 0; ii < PH; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int i = PH * ph + ii, c = b_row(j) + lcol;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = 32 * PH * wm + 32 * ii + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          cband[q * CPAD + c] = acc[i][j][r];
+        }
+      }
     __syncthreads();
-    auto tile_row = [&](int q) __attribute__((always_inline)) { return (q >> 5) * TM + 32 * i + (q & 31); };
     if constexpr (MODE == X_UP) {
       // 16 lanes per row, 8 gate + 8 up columns each; 4 lanes form one 32-column block of As
-      for (int id = tid; id < 64 * (CH / 2); id += NTH) {
+      for (int id = tid; id < BR * (CH / 2); id += NTH) {
         const int q = id / (CH / 2), cc = id % (CH / 2);
         const int lr = tile_row(q);
         const bool ok = lr < mrows;
@@ -334,20 +356,19 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
       }
     } else if constexpr (MODE == X_DACT) {
       // 32 lanes per row (8 columns each): dSwiGLU, routing-weight partial, dH in bf16 and MXFP8
-      for (int id = tid; id < 64 * CH; id += NTH) {
-        const int q = id / CH, cc = id % CH;
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int id = tid + it * NTH, q = id / CH, cc = id % CH;
         const int lr = tile_row(q);
         const bool ok = lr < mrows;
         const int64_t pos = m0 + (ok ? lr : 0);
         const int col = n0 + cc * 8;
-        const uint4 hgv = *(const uint4*)&g.Hs[pos * g.ldh + col];
-        const uint4 huv = *(const uint4*)&g.Hs[pos * g.ldh + g.f + col];
         const float* Gp = &cband[q * CPAD + cc * 8];
         const float w = s_w[lr];
         float part = 0.0f, dg[8], du[8];
 #pragma unroll
         for (int t2 = 0; t2 < 4; ++t2) {
-          const uint32_t wg = word_of(hgv, t2), wu = word_of(huv, t2);
+          const uint32_t wg = word_of(hgv[it], t2), wu = word_of(huv[it], t2);
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const float gv = hh ? hi_bf16(wg) : lo_bf16(wg), uv = hh ? hi_bf16(wu) : lo_bf16(wu);
@@ -378,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
         }
       }
     } else {
-      for (int id = tid; id < 64 * CH; id += NTH) {
+      for (int id = tid; id < BR * CH; id += NTH) {
         const int q = id / CH, cc = id % CH;
         const int lr = tile_row(q);
         if (lr < mrows) {
