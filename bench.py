@@ -76,7 +76,8 @@ STAGE_KERNEL_MX = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_mx_kernel<0
                        gemm_down="moe::grouped_gemm_mx_kernel<1>", gemm_dact="moe::grouped_gemm_mx_kernel<2>",
                        gemm_dx="moe::grouped_gemm_mx_kernel<3>", gemm_dw2="moe::grouped_gemm_mx_wg_kernel<0>",
                        gemm_dw1="moe::grouped_gemm_mx_wg_kernel<1>", mx_quant_t="moe::mx_quant_tokens",
-                       mx_pad="moe::mx_pad_offsets", mx_quant="moe::mx_quant_")
+                       mx_pad="moe::mx_pad_offsets", mx_quant="moe::mx_quant_",
+                       mx_exps="moe::mx_exps_sort")
 MX_FP8_STAGES = FP8_STAGES + ("gemm_dw2", "gemm_dw1")
 
 
@@ -122,6 +123,8 @@ def stage_bytes(stage, T, d, f, E, k, A):
         return A * 2 * f * 2 + A * 2 * f + A * 2 * f // 32
     if stage in ("mx_quant_x_t", "mx_quant_dy_t"):           # each token row read once, A rows out
         return T * d * 2 + A * d + A * d // 32
+    if stage in ("mx_exps_x", "mx_exps_dy"):                 # token-major exponents in, sorted words out
+        return T * d // 32 + A * 4 + A * d // 32
     if stage in ("mx_quant_w1", "mx_quant_w2"):
         return E * d * f * (2 + 1) + E * d * f // 32     # one of W1 (2df) / W2 (df): bytes of W1 halved
     return None

@@ -58,11 +58,11 @@ MoeShape shape_of(const moe_dims* d) {
 // for the weight gradients poff (padded expert offsets) and tqa/tea, tqb/teb (the two operands
 // of one product quantised along the token axis, reused by dW2 and then dW1).
 struct FwdLayout {
-  size_t tiles, ntiles, op, asq, ass, xq, xe, w1q, w1e, w2q, w2e, total;
+  size_t tiles, ntiles, op, asq, ass, xq, xe, xes, w1q, w1e, w2q, w2e, total;
 };
 struct BwdLayout {
-  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dHq, dHs, xbf, w1q,
-      w1e, w2q, w2e, poff, tqa, tea, tqb, teb, total;
+  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dyes, dHq, dHs, xbf,
+      w1q, w1e, w2q, w2e, poff, tqa, tea, tqb, teb, total;
   int max_partials;
 };
 // MXFP8 adds W1 and W2 quantised along the data gradients' K (row blocks), produced by the
@@ -97,6 +97,8 @@ FwdLayout fwd_layout(const moe_dims* d) {
     off += al256(T * dd);
     L.xe = off;
     off += al256(T * (dd / 32));
+    L.xes = off;  // x's exponents in the sorted order
+    off += al256((size_t)A * (dd / 32));
     L.w1q = off;
     off += al256(E * dd * 2 * ff);
     L.w1e = off;
@@ -153,6 +155,8 @@ BwdLayout bwd_layout(const moe_dims* d) {
     off += al256(T * dd);
     L.dys = off;
     off += al256(T * (dd / 32));
+    L.dyes = off;  // dy's exponents in the sorted order
+    off += al256((size_t)A * (dd / 32));
     L.dHq = off;
     off += al256((size_t)A * 2 * ff);
     L.dHs = off;
@@ -374,7 +378,7 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
   hipStream_t st = (hipStream_t)stream;
   if (is_mx(dims)) {
     uint8_t *Asq = (uint8_t*)(w + L.asq), *Ase = (uint8_t*)(w + L.ass);
-    uint8_t *xq = (uint8_t*)(w + L.xq), *xe = (uint8_t*)(w + L.xe);
+    uint8_t *xq = (uint8_t*)(w + L.xq), *xe = (uint8_t*)(w + L.xe), *xes = (uint8_t*)(w + L.xes);
     uint8_t *w1q = (uint8_t*)(w + L.w1q), *w1e = (uint8_t*)(w + L.w1e);
     uint8_t *w2q = (uint8_t*)(w + L.w2q), *w2e = (uint8_t*)(w + L.w2e);
     uint8_t *w1bq = (uint8_t*)(sv + SL.w1q), *w1be = (uint8_t*)(sv + SL.w1e);
@@ -385,7 +389,8 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
     MOE_TRY("mx_quant_w1", launch_mx_quant_dual((const uint16_t*)W1, s.E, s.d, 2 * s.f, w1q, w1e, w1bq, w1be, st));
     MOE_TRY("mx_quant_w2", launch_mx_quant_dual((const uint16_t*)W2, s.E, s.f, s.d, w2q, w2e, w2bq, w2be, st));
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
-    MOE_TRY("gemm_up", launch_mx_up(s, xq, xe, w1q, w1e, topk_w, offsets, perm, tiles, ntiles, H, As, Asq, Ase, st));
+    MOE_TRY("mx_exps_x", launch_mx_exps_sort(xe, s.d, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, xes, st));
+    MOE_TRY("gemm_up", launch_mx_up(s, xq, xes, w1q, w1e, topk_w, offsets, perm, tiles, ntiles, H, As, Asq, Ase, st));
     MOE_TRY("gemm_down", launch_mx_down(s, Asq, Ase, w2q, w2e, offsets, perm, tiles, ntiles, Op, st));
     MOE_TRY("combine", launch_combine(Op, inv_perm, s.T, s.d, s.k, (uint16_t*)y, st));
     return MOE_OK;
@@ -509,14 +514,15 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   hipStream_t st = (hipStream_t)stream;
   const WgSplit sp = wg_split_of(L, w, offsets);
   if (is_mx(dims)) {
-    uint8_t *dyq = (uint8_t*)(w + L.dyq), *dye = (uint8_t*)(w + L.dys);
+    uint8_t *dyq = (uint8_t*)(w + L.dyq), *dye = (uint8_t*)(w + L.dys), *dyes = (uint8_t*)(w + L.dyes);
     uint8_t *dHq = (uint8_t*)(w + L.dHq), *dHe = (uint8_t*)(w + L.dHs);
     // W1, W2 in row blocks (K = 2f and d), quantised by the forward
     const uint8_t *w1q = (const uint8_t*)(sv + SL.w1q), *w1e = (const uint8_t*)(sv + SL.w1e);
     const uint8_t *w2q = (const uint8_t*)(sv + SL.w2q), *w2e = (const uint8_t*)(sv + SL.w2e);
     MOE_TRY("mx_quant_dy", launch_mx_quant((const uint16_t*)dy, 1, s.T, s.d, 0, dyq, dye, st));
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
-    MOE_TRY("gemm_dact", launch_mx_dact(s, dyq, dye, w2q, w2e, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq, dHe,
+    MOE_TRY("mx_exps_dy", launch_mx_exps_sort(dye, s.d, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, dyes, st));
+    MOE_TRY("gemm_dact", launch_mx_dact(s, dyq, dyes, w2q, w2e, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq, dHe,
                                         dwp, st));
     MOE_TRY("gemm_dx", launch_mx_dx(s, dHq, dHe, w1q, w1e, offsets, perm, tiles, ntiles, dXp, st));
     MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));

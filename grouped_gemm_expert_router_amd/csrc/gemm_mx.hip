@@ -27,15 +27,19 @@ enum MxMode { X_UP = 0, X_DOWN = 1, X_DACT = 2, X_DX = 3 };
 #define MX_GM 8
 #endif
 
+// Exponents of a row-blocked (KM) operand are kept by k step: the 32-bit word (t, r) at
+// byte 4 * (t * R + r) holds the E8M0 bytes of k blocks 4t .. 4t+3 of row r (R rows, K/128
+// steps).  A 128-deep step of a tile then takes its rows' exponents from one contiguous run
+// (128 bytes per 32 rows) instead of one cache line per row.
 struct MxArgs {
   const uint8_t* A;   // e4m3 rows, K contiguous
   int64_t lda;        // bytes
-  const uint8_t* Ae;  // E8M0 [rows, K/32]
-  int64_t lde_a;
+  const uint8_t* Ae;  // E8M0 words by k step, rows in the experts' sorted order
+  int64_t ae_kstride;  // bytes from one k step's words to the next (4 * rows of the buffer)
   const uint8_t* B;   // e4m3 weights of all experts
   int64_t ldb, b_estride;
-  const uint8_t* Be;  // E8M0 per expert: KN weights [K/32, N], KM weights [N, K/32]
-  int64_t lde_b, be_estride;
+  const uint8_t* Be;  // E8M0 per expert: KN weights [K/32, N] bytes, KM weights words by k step
+  int64_t lde_b, be_estride;  // KN: bytes per exponent row; KM: bytes per k step (4 N)
   int N, K, kslots, f;
   const int32_t* offsets;
   const int32_t* perm;
@@ -49,8 +53,8 @@ struct MxArgs {
   int64_t ldc1;
   uint8_t* Q;   // requantised output codes (UP: As, DACT: dH)
   int64_t ldq;
-  uint8_t* Qe;  // their E8M0 exponents, one per 32 columns
-  int64_t ldqe;
+  uint8_t* Qe;  // their E8M0 exponents, one per 32 columns, words by k step as Ae
+  int64_t qe_kstride;
   const uint16_t* Hs;
   int64_t ldh;
   float* dwp;  // d_topk_w partials, part-major: dwp[part * dwp_stride + pos]
@@ -144,14 +148,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
     const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
     a_src[q] = g.A + src * g.lda + 16 * c;
   }
-  // A exponents: wave w brings the 4 bytes (k blocks of the stage) of rows 32w..32w+31; lanes
-  // past 31 repeat row 32w + 31.
+  // A exponents: wave w brings the word (k blocks of the stage) of rows 32w..32w+31, 128
+  // contiguous bytes of the sorted order; lanes past 31 repeat row 32w + 31.
   const uint8_t* ae_src;
   {
     const int row = 32 * wave + min(lane, 31);
-    const int pos = m0 + (row < mrows ? row : 0);
-    const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
-    ae_src = g.Ae + src * g.lde_a;
+    ae_src = g.Ae + (int64_t)(m0 + (row < mrows ? row : 0)) * 4;
   }
   const uint8_t* b_src[QB];
 #pragma unroll
@@ -170,7 +172,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
     }
   }
   // B exponents.  KN: rows kb = 4t..4t+3 of [K/32, N], 256 tile columns each; wave w < 4 brings
-  // row w, lane l columns 4l..4l+3 (UP: lanes < 32 gate, others up).  KM: like A, rows of W.
+  // row w, lane l columns 4l..4l+3 (UP: lanes < 32 gate, others up).  KM: like A, the words of
+  // W's rows n0 + 32w ..
   const uint8_t* be_src;
   if constexpr (B_KN) {
     int col;
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
     else col = n0 + 4 * lane;
     be_src = Beexp + (int64_t)(wave & 3) * g.lde_b + col;
   } else {
-    be_src = Beexp + (int64_t)(n0 + 32 * wave + min(lane, 31)) * g.lde_b;
+    be_src = Beexp + (int64_t)(n0 + 32 * wave + min(lane, 31)) * 4;
   }
   auto issue = [&](int t, int st) __attribute__((always_inline)) {
     const int k0 = t * BK;
@@ -189,11 +192,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
 #pragma unroll
     for (int q = 0; q < QB; ++q)
       dma16(B_KN ? b_src[q] + (int64_t)k0 * g.ldb : b_src[q] + k0, bbase + (wave * QB + q) * 1024);
-    dma4(ae_src + 4 * t, aebase + wave * 256);
+    dma4(ae_src + (int64_t)t * g.ae_kstride, aebase + wave * 256);
     if constexpr (B_KN) {
       if (wave < 4) dma4(be_src + (int64_t)(4 * t) * g.lde_b, bebase + wave * 256);
     } else {
-      dma4(be_src + 4 * t, bebase + wave * 256);
+      dma4(be_src + (int64_t)t * g.lde_b, bebase + wave * 256);
     }
   };
 
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
           *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(hu[0], hu[1], hu[2], hu[3]);
           *(uint4*)&g.C1[pos * g.ldc1 + col] = make_uint4(ab[0], ab[1], ab[2], ab[3]);
           *(u32x2*)&g.Q[pos * g.ldq + col] = qv;
-          if ((cc & 3) == 0) g.Qe[pos * g.ldqe + col / 32] = (uint8_t)ex;
+          if ((cc & 3) == 0) g.Qe[(col >> 7) * g.qe_kstride + pos * 4 + ((col >> 5) & 3)] = (uint8_t)ex;
         }
       }
     } else if constexpr (MODE == X_DACT) {
@@ -392,8 +395,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_mx_kernel(const MxArgs g)
           *(u32x2*)&g.Q[pos * g.ldq + col] = qg;
           *(u32x2*)&g.Q[pos * g.ldq + g.f + col] = qu;
           if ((cc & 3) == 0) {
-            g.Qe[pos * g.ldqe + col / 32] = (uint8_t)eg;
-            g.Qe[pos * g.ldqe + (g.f + col) / 32] = (uint8_t)eu;
+            const int cu = g.f + col;
+            g.Qe[(col >> 7) * g.qe_kstride + pos * 4 + ((col >> 5) & 3)] = (uint8_t)eg;
+            g.Qe[(cu >> 7) * g.qe_kstride + pos * 4 + ((cu >> 5) & 3)] = (uint8_t)eu;
           }
           if (cc == 0) g.dwp[nt * g.dwp_stride + pos] = part;
         }
@@ -481,13 +485,14 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
 
 // Both orientations in one pass (a weight matrix read once): src bf16 [batch, rows, cols] ->
 // qc/qce in column blocks (exponents [batch, rows/32, cols]) and qr/qre in row blocks
-// (exponents [batch, rows, cols/32]).  One block of 256 threads per 32 x 256 tile: thread t owns
+// (exponents as words by k step, [batch, cols/128, rows] words).  One block of 256 threads per 32 x 256 tile: thread t owns
 // 4 rows (group t / 32) x 8 columns (chunk t % 32).  Row blocks: 4 neighbouring lanes.  Column
 // blocks: the 8 row groups' maxima meet in LDS.
 __global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __restrict__ src, int rows, int cols,
                                                             uint8_t* __restrict__ qc, uint8_t* __restrict__ qce,
                                                             uint8_t* __restrict__ qr, uint8_t* __restrict__ qre) {
   __shared__ float s_amax[8][256];
+  __shared__ uint8_t s_rex[32][8];  // row-block exponents of the tile: [row][block]
   const int t = threadIdx.x, cc = t & 31, rg = t >> 5;
   const int tiles_c = cols / 256, tiles_r = rows / 32;
   const int64_t b = blockIdx.x / (tiles_r * tiles_c);
@@ -501,14 +506,15 @@ __global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __re
     v[i][0] = lo_bf16(w.x); v[i][1] = hi_bf16(w.x); v[i][2] = lo_bf16(w.y); v[i][3] = hi_bf16(w.y);
     v[i][4] = lo_bf16(w.z); v[i][5] = hi_bf16(w.z); v[i][6] = lo_bf16(w.w); v[i][7] = hi_bf16(w.w);
   }
-  // row blocks (32 columns = 4 lanes)
+  // row blocks (32 columns = 4 lanes); their exponents meet in LDS and leave below as two runs
+  // of 32 words (one per k step of the tile's 256 columns)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t ex;
     const u32x2 q = mx_quant8_group4(v[i], &ex);
     const int64_t row = r0 + 4 * rg + i;
     *(u32x2*)(qr + mat + row * cols + c0) = q;
-    if ((cc & 3) == 0) qre[(b * rows + row) * (int64_t)(cols / 32) + c0 / 32] = (uint8_t)ex;
+    if ((cc & 3) == 0) s_rex[4 * rg + i][cc >> 2] = (uint8_t)ex;
   }
   // column blocks (32 rows = 8 row groups)
 #pragma unroll
@@ -519,6 +525,11 @@ __global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __re
     s_amax[rg][cc * 8 + c] = m;
   }
   __syncthreads();
+  if (t < 64) {
+    const int h = t >> 5, r = t & 31;
+    const int64_t kstep = (int64_t)(rem % tiles_c) * 2 + h;
+    *(uint32_t*)(qre + ((b * (cols / 128) + kstep) * rows + r0 + r) * 4) = *(const uint32_t*)&s_rex[r][4 * h];
+  }
   float inv[8];
   int sx[8];
 #pragma unroll
@@ -551,6 +562,45 @@ hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, in
   const int64_t blocks = batch * (rows / 32) * (cols / 256);
   if (blocks == 0) return hipSuccess;
   mx_quant_dual_kernel<<<(unsigned)blocks, 256, 0, st>>>(src, rows, cols, qc, qce, qr, qre);
+  return hipGetLastError();
+}
+
+// Exponent words of a token-major row-block quantisation (src: [T, nk] words, nk = K/128) in
+// the experts' sorted order, by k step: out word (t, pos) = src word t of token perm[pos] /
+// kslots, for every sorted position pos < offsets[E]; the buffer has rows_cap rows per k step.
+// One thread per (sorted position, four k steps blockIdx.y): one 16-byte load of the token's
+// words when nk % 4 == 0 (rows then stay 16-byte aligned), else four word loads.
+__global__ __launch_bounds__(256) void mx_exps_sort_kernel(const uint32_t* __restrict__ src, int nk,
+                                                           const int32_t* __restrict__ perm, int kslots,
+                                                           const int32_t* __restrict__ offsets, int E,
+                                                           int64_t rows_cap, uint32_t* __restrict__ out) {
+  const int64_t pos = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (pos >= offsets[E]) return;
+  const int t0 = 4 * blockIdx.y;
+  const uint32_t* row = src + (int64_t)(perm[pos] / kslots) * nk;
+  uint32_t w[4];
+  if (nk % 4 == 0) {
+    const uint4 v = *(const uint4*)(row + t0);
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = t0 + j < nk ? row[t0 + j] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (t0 + j < nk) out[(t0 + j) * rows_cap + pos] = w[j];
+}
+
+hipError_t launch_mx_exps_sort(const uint8_t* src, int K, const int32_t* perm, int kslots, const int32_t* offsets,
+                               int E, int64_t rows_cap, uint8_t* out, hipStream_t st) {
+  if (rows_cap == 0 || K == 0) return hipSuccess;
+  const int nk = K / 128;
+  const dim3 grid((unsigned)((rows_cap + 255) / 256), (unsigned)((nk + 3) / 4));
+  mx_exps_sort_kernel<<<grid, 256, 0, st>>>((const uint32_t*)src, nk, perm, kslots, offsets, E, rows_cap,
+                                            (uint32_t*)out);
   return hipGetLastError();
 }
 
@@ -596,8 +646,8 @@ hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe,
   MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
   g.A = xq;
   g.lda = s.d;
-  g.Ae = xe;
-  g.lde_a = s.d / 32;
+  g.Ae = xe;  // sorted by mx_exps_sort
+  g.ae_kstride = 4 * (int64_t)s.T * s.k;
   g.gatherA = 1;
   g.B = W1q;  // [E, d, 2f], column blocks: exponents [E, d/32, 2f]
   g.ldb = 2 * (int64_t)s.f;
@@ -615,7 +665,7 @@ hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe,
   g.Q = Asq;
   g.ldq = s.f;
   g.Qe = Ase;
-  g.ldqe = s.f / 32;
+  g.qe_kstride = 4 * (int64_t)s.T * s.k;
   return run_mx<X_UP>(g, (int64_t)s.T * s.k, s.E, s.f / 128, st);
 }
 
@@ -626,7 +676,7 @@ hipError_t launch_mx_down(const MoeShape& s, const uint8_t* Asq, const uint8_t* 
   g.A = Asq;
   g.lda = s.f;
   g.Ae = Ase;
-  g.lde_a = s.f / 32;
+  g.ae_kstride = 4 * (int64_t)s.T * s.k;
   g.B = W2q;  // [E, f, d], column blocks: exponents [E, f/32, d]
   g.ldb = s.d;
   g.b_estride = (int64_t)s.f * s.d;
@@ -647,14 +697,14 @@ hipError_t launch_mx_dact(const MoeShape& s, const uint8_t* dyq, const uint8_t* 
   MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
   g.A = dyq;
   g.lda = s.d;
-  g.Ae = dye;
-  g.lde_a = s.d / 32;
+  g.Ae = dye;  // sorted by mx_exps_sort
+  g.ae_kstride = 4 * (int64_t)s.T * s.k;
   g.gatherA = 1;
-  g.B = W2q;  // [E, f, d], row blocks (K = d): exponents [E, f, d/32]
+  g.B = W2q;  // [E, f, d], row blocks (K = d): exponent words [E, d/128, f]
   g.ldb = s.d;
   g.b_estride = (int64_t)s.f * s.d;
   g.Be = W2e;
-  g.lde_b = s.d / 32;
+  g.lde_b = 4 * (int64_t)s.f;
   g.be_estride = (int64_t)s.f * (s.d / 32);
   g.N = s.f;
   g.K = s.d;
@@ -666,7 +716,7 @@ hipError_t launch_mx_dact(const MoeShape& s, const uint8_t* dyq, const uint8_t* 
   g.Q = dHq;
   g.ldq = 2 * (int64_t)s.f;
   g.Qe = dHe;
-  g.ldqe = 2 * s.f / 32;
+  g.qe_kstride = 4 * (int64_t)s.T * s.k;
   g.dwp = dwp;
   g.dwp_stride = (int64_t)s.T * s.k;  // one partial per 256-column N tile
   return run_mx<X_DACT>(g, (int64_t)s.T * s.k, s.E, s.f / 256, st);
@@ -679,12 +729,12 @@ hipError_t launch_mx_dx(const MoeShape& s, const uint8_t* dHq, const uint8_t* dH
   g.A = dHq;
   g.lda = 2 * (int64_t)s.f;
   g.Ae = dHe;
-  g.lde_a = 2 * s.f / 32;
-  g.B = W1q;  // [E, d, 2f], row blocks (K = 2f): exponents [E, d, 2f/32]
+  g.ae_kstride = 4 * (int64_t)s.T * s.k;
+  g.B = W1q;  // [E, d, 2f], row blocks (K = 2f): exponent words [E, 2f/128, d]
   g.ldb = 2 * (int64_t)s.f;
   g.b_estride = (int64_t)s.d * 2 * s.f;
   g.Be = W1e;
-  g.lde_b = 2 * s.f / 32;
+  g.lde_b = 4 * (int64_t)s.d;
   g.be_estride = (int64_t)s.d * (2 * s.f / 32);
   g.N = s.d;
   g.K = 2 * s.f;

@@ -109,7 +109,8 @@ hipError_t launch_dequant_rows(const uint8_t* q, const float* qs, int64_t rows, 
 hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int cols, int along_rows, uint8_t* q,
                            uint8_t* qe, hipStream_t st);
 // Both orientations of [batch, rows, cols] in one pass (rows % 32 == 0, cols % 256 == 0):
-// column blocks into qc/qce, row blocks into qr/qre.
+// column blocks into qc/qce, row blocks into qr with their exponents as 32-bit words by k step
+// in qre ([batch, cols/128, rows] words: word (t, r) = the exponents of blocks 4t..4t+3 of row r).
 // MXFP8 weight gradients: each expert's rows padded to a multiple of 128 (see gemm_mx.hip).
 inline int64_t mx_padded_rows(int64_t A, int E) { return (A + 127 * (int64_t)E + 127) / 128 * 128; }
 hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t st);
@@ -122,6 +123,13 @@ hipError_t launch_mx_wg(int which, const MoeShape& s, const uint8_t* Aq, const u
                         hipStream_t st);
 hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, int cols, uint8_t* qc, uint8_t* qce,
                                 uint8_t* qr, uint8_t* qre, hipStream_t st);
+// Row-block exponents of token rows ([T, K/32] bytes) as words by k step in the experts' sorted
+// order: out word (t, pos) at byte 4 * (t * rows_cap + pos), from token perm[pos] / kslots.
+hipError_t launch_mx_exps_sort(const uint8_t* src, int K, const int32_t* perm, int kslots, const int32_t* offsets,
+                               int E, int64_t rows_cap, uint8_t* out, hipStream_t st);
+// The MX GEMMs take every row-blocked operand's exponents as words by k step: x and dy sorted
+// by launch_mx_exps_sort, As and dH as the epilogues write them, W1/W2 as launch_mx_quant_dual's
+// row-block output.
 hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe, const uint8_t* W1q,
                         const uint8_t* W1e, const float* topk_w, const int32_t* offsets, const int32_t* perm,
                         const int2* tiles, const int32_t* ntiles, uint16_t* H, uint16_t* As, uint8_t* Asq,
