@@ -54,7 +54,8 @@ STAGE_KERNEL_BF16 = {"gemm_up": "moe::grouped_gemm_kernel<0,", "gemm_down": "moe
                      "dlogits": "moe::dlogits_kernel", "wg_reduce": "moe::wg_reduce_kernel",
                      "plan": "moe::plan_", "tile_map": "moe::tile_map_kernel", "wg_split": "moe::wg_split_kernel",
                      "tokrow": "moe::tokrow_kernel", "permute": "moe::permute_kernel",
-                     "gemm_fused": "moe::fused_forward_kernel", "fwd_queue": "moe::fwd_queue_kernel"}
+                     "gemm_fused": "moe::fused_forward_kernel", "fwd_queue": "moe::fwd_queue_kernel",
+                     "ksort": "moe::kstep_sort_kernel"}
 # blockwise fp8: the four data GEMMs in e4m3, the weight gradients in bf16 on x dequantised to bf16
 STAGE_KERNEL_FP8 = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_fp8_kernel<0>",
                         gemm_down="moe::grouped_gemm_fp8_kernel<1>", gemm_dact="moe::grouped_gemm_fp8_kernel<2>",
@@ -76,8 +77,7 @@ STAGE_KERNEL_MX = dict(STAGE_KERNEL_BF16, gemm_up="moe::grouped_gemm_mx_kernel<0
                        gemm_down="moe::grouped_gemm_mx_kernel<1>", gemm_dact="moe::grouped_gemm_mx_kernel<2>",
                        gemm_dx="moe::grouped_gemm_mx_kernel<3>", gemm_dw2="moe::grouped_gemm_mx_wg_kernel<0>",
                        gemm_dw1="moe::grouped_gemm_mx_wg_kernel<1>", mx_quant_t="moe::mx_quant_tokens",
-                       mx_pad="moe::mx_pad_offsets", mx_quant="moe::mx_quant_",
-                       mx_exps="moe::mx_exps_sort")
+                       mx_pad="moe::mx_pad_offsets", mx_quant="moe::mx_quant_")
 MX_FP8_STAGES = FP8_STAGES + ("gemm_dw2", "gemm_dw1")
 
 
@@ -123,7 +123,7 @@ def stage_bytes(stage, T, d, f, E, k, A):
         return A * 2 * f * 2 + A * 2 * f + A * 2 * f // 32
     if stage in ("mx_quant_x_t", "mx_quant_dy_t"):           # each token row read once, A rows out
         return T * d * 2 + A * d + A * d // 32
-    if stage in ("mx_exps_x", "mx_exps_dy"):                 # token-major exponents in, sorted words out
+    if stage in ("ksort_x", "ksort_dy"):    # token-major words (d/32 bytes a row) in, sorted by k step out
         return T * d // 32 + A * 4 + A * d // 32
     if stage in ("mx_quant_w1", "mx_quant_w2"):
         return E * d * f * (2 + 1) + E * d * f // 32     # one of W1 (2df) / W2 (df): bytes of W1 halved

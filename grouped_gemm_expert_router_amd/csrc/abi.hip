@@ -58,10 +58,10 @@ MoeShape shape_of(const moe_dims* d) {
 // for the weight gradients poff (padded expert offsets) and tqa/tea, tqb/teb (the two operands
 // of one product quantised along the token axis, reused by dW2 and then dW1).
 struct FwdLayout {
-  size_t tiles, ntiles, op, asq, ass, xq, xe, xes, w1q, w1e, w2q, w2e, total;
+  size_t tiles, ntiles, op, asq, ass, xss, xq, xe, xes, w1q, w1e, w2q, w2e, total;
 };
 struct BwdLayout {
-  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dyes, dHq, dHs, xbf,
+  size_t tiles, ntiles, tokrow, dH, dXp, dwp, wg_units, wg_meta, wg_pslot, wg_partial, dyq, dys, dyss, dyes, dHq, dHs, xbf,
       w1q, w1e, w2q, w2e, poff, tqa, tea, tqb, teb, total;
   int max_partials;
 };
@@ -86,6 +86,8 @@ FwdLayout fwd_layout(const moe_dims* d) {
     off += al256((size_t)A * d->f);
     L.ass = off;
     off += al256((size_t)A * (d->f / 128) * sizeof(float));
+    L.xss = off;  // x's row scales in the sorted order, by k block
+    off += al256((size_t)A * (d->d / 128) * sizeof(float));
   }
   if (is_mx(d)) {
     const size_t E = d->E, dd = d->d, ff = d->f, T = d->T;
@@ -142,6 +144,8 @@ BwdLayout bwd_layout(const moe_dims* d) {
     off += al256((size_t)d->T * d->d);
     L.dys = off;
     off += al256((size_t)d->T * (d->d / 128) * sizeof(float));
+    L.dyss = off;  // dy's row scales in the sorted order, by k block
+    off += al256((size_t)A * (d->d / 128) * sizeof(float));
     L.dHq = off;
     off += al256((size_t)A * 2 * d->f);
     L.dHs = off;
@@ -389,7 +393,7 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
     MOE_TRY("mx_quant_w1", launch_mx_quant_dual((const uint16_t*)W1, s.E, s.d, 2 * s.f, w1q, w1e, w1bq, w1be, st));
     MOE_TRY("mx_quant_w2", launch_mx_quant_dual((const uint16_t*)W2, s.E, s.f, s.d, w2q, w2e, w2bq, w2be, st));
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
-    MOE_TRY("mx_exps_x", launch_mx_exps_sort(xe, s.d, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, xes, st));
+    MOE_TRY("ksort_x", launch_kstep_sort(xe, s.d / 128, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, xes, st));
     MOE_TRY("gemm_up", launch_mx_up(s, xq, xes, w1q, w1e, topk_w, offsets, perm, tiles, ntiles, H, As, Asq, Ase, st));
     MOE_TRY("gemm_down", launch_mx_down(s, Asq, Ase, w2q, w2e, offsets, perm, tiles, ntiles, Op, st));
     MOE_TRY("combine", launch_combine(Op, inv_perm, s.T, s.d, s.k, (uint16_t*)y, st));
@@ -398,9 +402,11 @@ int moe_forward(const moe_dims* dims, const void* x, const float* x_scale, const
   if (fp8) {
     uint8_t* Asq = (uint8_t*)(w + L.asq);
     float* Ass = (float*)(w + L.ass);
+    float* xss = (float*)(w + L.xss);
     const uint8_t *x8 = (const uint8_t*)x, *W18 = (const uint8_t*)W1, *W28 = (const uint8_t*)W2;
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
-    MOE_TRY("gemm_up", launch_fp8_up(s, x8, x_scale, W18, W1_scale, topk_w, offsets, perm, tiles, ntiles, H, As, Asq,
+    MOE_TRY("ksort_x", launch_kstep_sort(x_scale, s.d / 128, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, xss, st));
+    MOE_TRY("gemm_up", launch_fp8_up(s, x8, xss, W18, W1_scale, topk_w, offsets, perm, tiles, ntiles, H, As, Asq,
                                      Ass, st));
     MOE_TRY("gemm_down", launch_fp8_down(s, Asq, Ass, W28, W2_scale, offsets, perm, tiles, ntiles, Op, st));
     MOE_TRY("combine", launch_combine(Op, inv_perm, s.T, s.d, s.k, (uint16_t*)y, st));
@@ -521,7 +527,7 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
     const uint8_t *w2q = (const uint8_t*)(sv + SL.w2q), *w2e = (const uint8_t*)(sv + SL.w2e);
     MOE_TRY("mx_quant_dy", launch_mx_quant((const uint16_t*)dy, 1, s.T, s.d, 0, dyq, dye, st));
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
-    MOE_TRY("mx_exps_dy", launch_mx_exps_sort(dye, s.d, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, dyes, st));
+    MOE_TRY("ksort_dy", launch_kstep_sort(dye, s.d / 128, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, dyes, st));
     MOE_TRY("gemm_dact", launch_mx_dact(s, dyq, dyes, w2q, w2e, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq, dHe,
                                         dwp, st));
     MOE_TRY("gemm_dx", launch_mx_dx(s, dHq, dHe, w1q, w1e, offsets, perm, tiles, ntiles, dXp, st));
@@ -536,12 +542,14 @@ int moe_backward(const moe_dims* dims, const void* dy, const void* x, const floa
   if (fp8) {
     uint8_t* dyq = (uint8_t*)(w + L.dyq);
     float* dys = (float*)(w + L.dys);
+    float* dyss = (float*)(w + L.dyss);
     uint8_t* dHq = (uint8_t*)(w + L.dHq);
     float* dHs = (float*)(w + L.dHs);
     const uint8_t *W18 = (const uint8_t*)W1, *W28 = (const uint8_t*)W2;
     MOE_TRY("quant_dy", launch_quant_rows((const uint16_t*)dy, s.T, s.d, dyq, dys, st));
     MOE_TRY("tile_map", launch_tile_map(offsets, s.E, kFp8BM, tiles, ntiles, st));
-    MOE_TRY("gemm_dact", launch_fp8_dact(s, dyq, dys, W28, W2_scale, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq,
+    MOE_TRY("ksort_dy", launch_kstep_sort(dys, s.d / 128, perm, s.k, offsets, s.E, (int64_t)s.T * s.k, dyss, st));
+    MOE_TRY("gemm_dact", launch_fp8_dact(s, dyq, dyss, W28, W2_scale, H, topk_w, offsets, perm, tiles, ntiles, dH, dHq,
                                          dHs, dwp, st));
     MOE_TRY("gemm_dx", launch_fp8_dx(s, dHq, dHs, W18, W1_scale, offsets, perm, tiles, ntiles, dXp, st));
     MOE_TRY("combine_dx", launch_combine(dXp, inv_perm, s.T, s.d, s.k, (uint16_t*)dx, st));

@@ -35,6 +35,45 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* inv_perm, int T, int
   return hipGetLastError();
 }
 
+// Per-row words of token rows, one per 128-wide k step (MXFP8 exponent words, fp8 row scales),
+// into the experts' sorted order, k-step-major: out[t * rows_cap + pos] = src[token * nk + t]
+// with token = perm[pos] / kslots, for every sorted position pos < offsets[E].  A GEMM tile's
+// k step then finds the words of its rows in one contiguous run instead of one line per row.
+// One thread per (sorted position, four k steps blockIdx.y): one 16-byte load of the token's
+// words when nk % 4 == 0 (rows then stay 16-byte aligned), else up to four word loads.
+__global__ __launch_bounds__(256) void kstep_sort_kernel(const uint32_t* __restrict__ src, int nk,
+                                                         const int32_t* __restrict__ perm, int kslots,
+                                                         const int32_t* __restrict__ offsets, int E,
+                                                         int64_t rows_cap, uint32_t* __restrict__ out) {
+  const int64_t pos = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (pos >= offsets[E]) return;
+  const int t0 = 4 * blockIdx.y;
+  const uint32_t* row = src + (int64_t)(perm[pos] / kslots) * nk;
+  uint32_t w[4];
+  if (nk % 4 == 0) {
+    const uint4 v = *(const uint4*)(row + t0);
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = t0 + j < nk ? row[t0 + j] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (t0 + j < nk) out[(t0 + j) * rows_cap + pos] = w[j];
+}
+
+hipError_t launch_kstep_sort(const void* src, int nk, const int32_t* perm, int kslots, const int32_t* offsets, int E,
+                             int64_t rows_cap, void* out, hipStream_t st) {
+  if (rows_cap == 0 || nk == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows_cap + 255) / 256), (unsigned)((nk + 3) / 4));
+  kstep_sort_kernel<<<grid, 256, 0, st>>>((const uint32_t*)src, nk, perm, kslots, offsets, E, rows_cap,
+                                          (uint32_t*)out);
+  return hipGetLastError();
+}
+
 // y[t] = bf16( sum_{j=0..k-1, inv_perm[t*k+j] >= 0} op[t*k+j] ) with an fp32 running sum.
 // The slots are taken 4 at a time: their row loads are all issued before the first add, and
 // the adds then run in slot order.  The per-pair rows are read once (non-temporal loads).

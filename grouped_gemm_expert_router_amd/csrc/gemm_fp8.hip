@@ -33,8 +33,8 @@ enum Fp8Mode { F_UP = 0, F_DOWN = 1, F_DACT = 2, F_DX = 3 };
 struct Fp8Args {
   const uint8_t* A;        // fp8 rows, K contiguous
   int64_t lda;             // bytes
-  const float* A_scale;    // [rows, K/128]
-  int64_t lds_a;           // floats per scale row
+  const float* A_scale;    // by k step: the scale of sorted row pos for k block t at t * as_kstride + pos
+  int as_kstride;          // floats from one k block's scales to the next (rows of the buffer)
   const uint8_t* B;        // fp8 weights of all experts
   int64_t ldb, b_estride;  // bytes
   const float* B_scale;    // per expert [rows/128, cols/128] of B as stored
@@ -53,8 +53,8 @@ struct Fp8Args {
   int64_t ldc1;
   uint8_t* Q;  // requantised output (UP: As, DACT: dH)
   int64_t ldq;
-  float* QS;
-  int64_t ldqs;
+  float* QS;  // their scales by k step, as A_scale
+  int64_t qs_kstride;
   const uint16_t* Hs;
   int64_t ldh;
   float* dwp;  // d_topk_w partials, part-major: dwp[part * dwp_stride + pos]
@@ -137,18 +137,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
     a_src[q] = g.A + src * g.lda + 16 * c;
   }
   // Scales of a K stage, one 4-byte DMA per wave into its 256-byte slot: lanes 0..31 bring the
-  // row scales of rows 32w..32w+31, lanes 32 and 33 the weight-block scales of the wave's two
-  // B fragments (lanes past 33 repeat lane 32).  Each lane's source advances by sc_step floats
-  // per stage.  With no scalar load in the K loop the stage's LDS reads retire in order, so each
+  // row scales of rows 32w..32w+31 (128 contiguous bytes: the row scales are stored by k step
+  // in the sorted order), lanes 32 and 33 the weight-block scales of the wave's two B fragments
+  // (lanes past 33 repeat lane 32).  Each lane's source advances by sc_step floats per stage.  With no scalar load in the K loop the stage's LDS reads retire in order, so each
   // MFMA waits only for its own fragments.
   const float* sc_src;
   int sc_step;
   if (lane < 32) {
     const int row = 32 * wave + lane;
-    const int pos = m0 + (row < mrows ? row : 0);
-    const int64_t src = g.gatherA ? (int64_t)(g.perm[pos] / g.kslots) : (int64_t)pos;
-    sc_src = g.A_scale + src * g.lds_a;
-    sc_step = 1;
+    sc_src = g.A_scale + (m0 + (row < mrows ? row : 0));
+    sc_step = g.as_kstride;
   } else {
     const int j = lane == 33 ? 1 : 0;
     int nb;  // 128-column block of the weight matrix holding B fragment j
@@ -359,7 +357,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
           *(uint4*)&g.C0[pos * g.ldc0 + g.f + col] = make_uint4(hu[0], hu[1], hu[2], hu[3]);
           *(uint4*)&g.C1[pos * g.ldc1 + col] = make_uint4(ab[0], ab[1], ab[2], ab[3]);
           *(u32x2*)&g.Q[pos * g.ldq + col] = qv;
-          if (cc == 0) g.QS[pos * g.ldqs + nt] = sc;
+          if (cc == 0) g.QS[nt * g.qs_kstride + pos] = sc;
         }
       }
     } else if constexpr (MODE == F_DACT) {
@@ -400,8 +398,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_fp8_kernel(const Fp8Args 
           *(u32x2*)&g.Q[pos * g.ldq + col] = qg;
           *(u32x2*)&g.Q[pos * g.ldq + g.f + col] = qu;
           if ((cc & 15) == 0) {
-            g.QS[pos * g.ldqs + col / 128] = sg_;
-            g.QS[pos * g.ldqs + (g.f + col) / 128] = su_;
+            g.QS[(col / 128) * g.qs_kstride + pos] = sg_;
+            g.QS[((g.f + col) / 128) * g.qs_kstride + pos] = su_;
           }
           if (cc == 0) g.dwp[nt * g.dwp_stride + pos] = part;
         }
@@ -450,8 +448,8 @@ hipError_t launch_fp8_up(const MoeShape& s, const uint8_t* x, const float* xs, c
   Fp8Args g = fp8_base(s, offsets, perm, tiles, ntiles);
   g.A = x;
   g.lda = s.d;
-  g.A_scale = xs;
-  g.lds_a = s.d / 128;
+  g.A_scale = xs;  // sorted by launch_kstep_sort
+  g.as_kstride = (int)(s.T * s.k);
   g.gatherA = 1;
   g.B = W1;
   g.ldb = 2 * (int64_t)s.f;
@@ -469,7 +467,7 @@ hipError_t launch_fp8_up(const MoeShape& s, const uint8_t* x, const float* xs, c
   g.Q = Asq;
   g.ldq = s.f;
   g.QS = Ass;
-  g.ldqs = s.f / 128;
+  g.qs_kstride = s.T * s.k;
   return run_fp8<F_UP>(g, (int64_t)s.T * s.k, s.E, s.f / 128, st);
 }
 
@@ -480,7 +478,7 @@ hipError_t launch_fp8_down(const MoeShape& s, const uint8_t* Asq, const float* A
   g.A = Asq;
   g.lda = s.f;
   g.A_scale = Ass;
-  g.lds_a = s.f / 128;
+  g.as_kstride = (int)(s.T * s.k);
   g.B = W2;
   g.ldb = s.d;
   g.b_estride = (int64_t)s.f * s.d;
@@ -501,8 +499,8 @@ hipError_t launch_fp8_dact(const MoeShape& s, const uint8_t* dyq, const float* d
   Fp8Args g = fp8_base(s, offsets, perm, tiles, ntiles);
   g.A = dyq;
   g.lda = s.d;
-  g.A_scale = dys;
-  g.lds_a = s.d / 128;
+  g.A_scale = dys;  // sorted by launch_kstep_sort
+  g.as_kstride = (int)(s.T * s.k);
   g.gatherA = 1;
   g.B = W2;  // row n of W2[e] ([f, d]) is column n of W2[e]^T, contiguous in K = d
   g.ldb = s.d;
@@ -520,7 +518,7 @@ hipError_t launch_fp8_dact(const MoeShape& s, const uint8_t* dyq, const float* d
   g.Q = dHq;
   g.ldq = 2 * (int64_t)s.f;
   g.QS = dHs;
-  g.ldqs = 2 * s.f / 128;
+  g.qs_kstride = s.T * s.k;
   g.dwp = dwp;
   g.dwp_stride = (int64_t)s.T * s.k;  // one partial per 256-column N tile
   return run_fp8<F_DACT>(g, (int64_t)s.T * s.k, s.E, s.f / 256, st);
@@ -533,7 +531,7 @@ hipError_t launch_fp8_dx(const MoeShape& s, const uint8_t* dHq, const float* dHs
   g.A = dHq;
   g.lda = 2 * (int64_t)s.f;
   g.A_scale = dHs;
-  g.lds_a = 2 * s.f / 128;
+  g.as_kstride = (int)(s.T * s.k);
   g.B = W1;  // row n of W1[e] ([d, 2f]) is column n of W1[e]^T, contiguous in K = 2f
   g.ldb = 2 * (int64_t)s.f;
   g.b_estride = (int64_t)s.d * 2 * s.f;

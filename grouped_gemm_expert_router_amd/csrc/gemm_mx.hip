@@ -565,45 +565,6 @@ hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, in
   return hipGetLastError();
 }
 
-// Exponent words of a token-major row-block quantisation (src: [T, nk] words, nk = K/128) in
-// the experts' sorted order, by k step: out word (t, pos) = src word t of token perm[pos] /
-// kslots, for every sorted position pos < offsets[E]; the buffer has rows_cap rows per k step.
-// One thread per (sorted position, four k steps blockIdx.y): one 16-byte load of the token's
-// words when nk % 4 == 0 (rows then stay 16-byte aligned), else four word loads.
-__global__ __launch_bounds__(256) void mx_exps_sort_kernel(const uint32_t* __restrict__ src, int nk,
-                                                           const int32_t* __restrict__ perm, int kslots,
-                                                           const int32_t* __restrict__ offsets, int E,
-                                                           int64_t rows_cap, uint32_t* __restrict__ out) {
-  const int64_t pos = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (pos >= offsets[E]) return;
-  const int t0 = 4 * blockIdx.y;
-  const uint32_t* row = src + (int64_t)(perm[pos] / kslots) * nk;
-  uint32_t w[4];
-  if (nk % 4 == 0) {
-    const uint4 v = *(const uint4*)(row + t0);
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = t0 + j < nk ? row[t0 + j] : 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (t0 + j < nk) out[(t0 + j) * rows_cap + pos] = w[j];
-}
-
-hipError_t launch_mx_exps_sort(const uint8_t* src, int K, const int32_t* perm, int kslots, const int32_t* offsets,
-                               int E, int64_t rows_cap, uint8_t* out, hipStream_t st) {
-  if (rows_cap == 0 || K == 0) return hipSuccess;
-  const int nk = K / 128;
-  const dim3 grid((unsigned)((rows_cap + 255) / 256), (unsigned)((nk + 3) / 4));
-  mx_exps_sort_kernel<<<grid, 256, 0, st>>>((const uint32_t*)src, nk, perm, kslots, offsets, E, rows_cap,
-                                            (uint32_t*)out);
-  return hipGetLastError();
-}
-
 hipError_t launch_mx_quant(const uint16_t* src, int64_t batch, int rows, int cols, int along_rows, uint8_t* q,
                            uint8_t* qe, hipStream_t st) {
   if (batch * rows * cols == 0) return hipSuccess;
@@ -646,7 +607,7 @@ hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe,
   MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
   g.A = xq;
   g.lda = s.d;
-  g.Ae = xe;  // sorted by mx_exps_sort
+  g.Ae = xe;  // sorted by launch_kstep_sort
   g.ae_kstride = 4 * (int64_t)s.T * s.k;
   g.gatherA = 1;
   g.B = W1q;  // [E, d, 2f], column blocks: exponents [E, d/32, 2f]
@@ -697,7 +658,7 @@ hipError_t launch_mx_dact(const MoeShape& s, const uint8_t* dyq, const uint8_t* 
   MxArgs g = mx_base(s, offsets, perm, tiles, ntiles);
   g.A = dyq;
   g.lda = s.d;
-  g.Ae = dye;  // sorted by mx_exps_sort
+  g.Ae = dye;  // sorted by launch_kstep_sort
   g.ae_kstride = 4 * (int64_t)s.T * s.k;
   g.gatherA = 1;
   g.B = W2q;  // [E, f, d], row blocks (K = d): exponent words [E, d/128, f]

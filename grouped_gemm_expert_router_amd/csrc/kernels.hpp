@@ -123,12 +123,8 @@ hipError_t launch_mx_wg(int which, const MoeShape& s, const uint8_t* Aq, const u
                         hipStream_t st);
 hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, int cols, uint8_t* qc, uint8_t* qce,
                                 uint8_t* qr, uint8_t* qre, hipStream_t st);
-// Row-block exponents of token rows ([T, K/32] bytes) as words by k step in the experts' sorted
-// order: out word (t, pos) at byte 4 * (t * rows_cap + pos), from token perm[pos] / kslots.
-hipError_t launch_mx_exps_sort(const uint8_t* src, int K, const int32_t* perm, int kslots, const int32_t* offsets,
-                               int E, int64_t rows_cap, uint8_t* out, hipStream_t st);
 // The MX GEMMs take every row-blocked operand's exponents as words by k step: x and dy sorted
-// by launch_mx_exps_sort, As and dH as the epilogues write them, W1/W2 as launch_mx_quant_dual's
+// by launch_kstep_sort, As and dH as the epilogues write them, W1/W2 as launch_mx_quant_dual's
 // row-block output.
 hipError_t launch_mx_up(const MoeShape& s, const uint8_t* xq, const uint8_t* xe, const uint8_t* W1q,
                         const uint8_t* W1e, const float* topk_w, const int32_t* offsets, const int32_t* perm,
@@ -158,6 +154,11 @@ hipError_t launch_router_dwg(const uint16_t* x, const float* d_logits, int T, in
                              float* partial, hipStream_t st);
 
 // data movement and router backward
+// Per-row words of token rows ([T, nk] 32-bit words, one per 128-wide k step) into the sorted
+// order by k step: out word (t, pos) at out + t * rows_cap + pos, from token perm[pos] / kslots,
+// for pos < offsets[E].
+hipError_t launch_kstep_sort(const void* src, int nk, const int32_t* perm, int kslots, const int32_t* offsets, int E,
+                             int64_t rows_cap, void* out, hipStream_t st);
 hipError_t launch_permute(const uint16_t* x, const int32_t* inv_perm, int T, int d, int k, uint16_t* xp,
                           hipStream_t st);
 hipError_t launch_combine(const uint16_t* op, const int32_t* inv_perm, int T, int d, int k, uint16_t* y,
