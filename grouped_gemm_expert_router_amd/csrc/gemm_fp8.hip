@@ -10,7 +10,8 @@
 // into a temporary, which is then promoted into the fp32 accumulator with s_a(row) * s_b(block).
 // Tiles are 256 x 256 x 128 with 8 waves (2 x 4), each owning 128 x 64.  Operands reach LDS by
 // DMA; K-contiguous tiles are read with ds_read_b128, N-contiguous weight tiles with the 8-bit
-// LDS transpose read.  The row scales of each stage arrive by DMA as well.
+// LDS transpose read.  The row scales of each stage arrive by DMA as well; they are stored by
+// k block in the experts' sorted order, so those of 32 rows are one contiguous run.
 //
 // Epilogues: UP writes H (bf16, kept for the backward), As = w * silu(g) * u in bf16 (for the
 // weight gradient) and requantised to e4m3 with one scale per row per 128 columns (the next

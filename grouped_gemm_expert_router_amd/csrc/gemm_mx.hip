@@ -12,7 +12,9 @@
 // row blocks (K = d), W1 and W2 in column blocks for the forward (K = d and f) and in row blocks
 // for the data gradients (K = 2f and d).  The epilogues requantise As (K = f of the down
 // projection) and dH (K = 2f of dX) the same way.  The block exponent is the smallest power of
-// two that brings the block's maximum magnitude within 448, so no element is clipped.
+// two that brings the block's maximum magnitude within 448, so no element is clipped.  The
+// exponents of a row-blocked operand are kept as 32-bit words by k step (see MxArgs), so a
+// stage's DMA reads those of 32 rows as one contiguous run.
 //
 // Tiles are 256 x 256 x 128 (four scale blocks per stage) with 8 waves (2 x 4) of 128 x 64.
 #include "common.hpp"
