@@ -9,17 +9,17 @@ import pytest
 import torch
 
 import grouped_gemm_expert_router_amd as moe
-from workloads import make_inputs
+from workloads import make_inputs, make_prerouted_fp8
 from moe_testlib import GpuLayer
 
 pytestmark = pytest.mark.gpu
 
-OUTS = ("topk_ids", "topk_w", "counts", "offsets", "perm", "inv_perm", "y", "dx", "dW1", "dW2", "d_topk_w",
-        "d_logits")
+ROUTE_OUTS = ("topk_ids", "topk_w")
+OUTS = ("counts", "offsets", "perm", "inv_perm", "y", "dx", "dW1", "dW2", "d_topk_w")
 
 
-def _poison(gl):
-    for name in OUTS:
+def _poison(gl, outs):
+    for name in outs:
         t = gl.b[name]
         if t.is_floating_point():
             t.fill_(float("nan"))
@@ -27,35 +27,49 @@ def _poison(gl):
             t.fill_(-7)
 
 
-def _snapshot(gl):
-    return {name: gl.b[name].clone() for name in OUTS}
+def _snapshot(gl, outs):
+    return {name: gl.b[name].clone() for name in outs}
 
 
-def _check(gl, ref, what):
-    for name in OUTS:
+def _check(gl, ref, what, outs):
+    A = int(ref["offsets"][-1].item())
+    for name in outs:
         a, b = ref[name], gl.b[name]
+        if name == "perm":  # entries past offsets[E] are unused (pairs routed elsewhere have none)
+            a, b = a[:A], b[:A]
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"{what}: {name} differs from the eager step"
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_step_graph_replays_match_eager(fused):
-    inp = make_inputs(300, 256, 256, 8, 2, seed=40)
-    print(f"[case] graph replay fused={fused}", flush=True)
-    gl = GpuLayer(inp)
+# bf16 routed from logits (also through the single-launch forward), bf16 inputs run as MXFP8,
+# and the pre-routed blockwise-fp8 share (plan instead of route, no logits)
+CASES = ["bf16", "bf16_fused", "mxfp8", "fp8"]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_step_graph_replays_match_eager(case):
+    if case == "fp8":
+        inp = make_prerouted_fp8(256, 16, 4, 256, 256, 4, 46, name="fp8_graph")
+        gl = GpuLayer(inp)
+    else:
+        inp = make_inputs(300, 256, 256, 8, 2, seed=40)
+        gl = GpuLayer(inp, dtype=moe.MOE_MXFP8 if case == "mxfp8" else None)
+    print(f"[case] graph replay {case}", flush=True)
     b = gl.b
+    routed = gl.logits is not None
+    outs = OUTS + (ROUTE_OUTS + ("d_logits",) if routed else ())
 
     def step():
         gl.route()
-        if fused:
+        if case == "bf16_fused":
             moe.moe_forward_fused(gl.dm, gl.x, gl.W1, gl.W2, b["topk_w"], b["offsets"], b["perm"], b["inv_perm"],
                                   b["y"], b["saved"], b["ws_fwd"])
         else:
             gl.forward()
-        gl.backward(with_logits=True)
+        gl.backward(with_logits=routed)
 
     step()
     torch.cuda.synchronize()
-    ref = _snapshot(gl)
+    ref = _snapshot(gl, outs)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -70,13 +84,13 @@ def test_step_graph_replays_match_eager(fused):
     torch.cuda.synchronize()
 
     for rep in range(3):
-        _poison(gl)
+        _poison(gl, outs)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        _check(gl, ref, f"replay {rep}")
+        _check(gl, ref, f"replay {rep}", outs)
         # eager work between replays: the same step, checked too
-        _poison(gl)
+        _poison(gl, outs)
         step()
         torch.cuda.synchronize()
-        _check(gl, ref, f"eager step after replay {rep}")
+        _check(gl, ref, f"eager step after replay {rep}", outs)
