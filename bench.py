@@ -16,6 +16,7 @@ Helpers that read rocprofv3 CSV output (CPU only, print a text summary):
     python bench.py --summarize-stats DIR --config C --command "..."
     python bench.py --summarize-counters FETCH_DIR WRITE_DIR --config C --command "..."
     python bench.py --summarize-mfma DIR --config C --command "..."
+    python bench.py --summarize-memory DIR --config C --command "..."
 """
 from __future__ import annotations
 
@@ -345,6 +346,42 @@ def summarize_mfma(d, config, command):
               f"{name.split('(')[0].replace('void ', '')}")
 
 
+MEMORY_COUNTERS = ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "TCC_TAG_STALL_sum",
+                   "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA_DATA_STALLED_BY_TC_CYCLES_sum",
+                   "TCP_PENDING_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE")
+
+
+def summarize_memory(d, config, command):
+    """Memory-side counters per GEMM: the L2 hit rate by request (TCC_HIT / (TCC_HIT + TCC_MISS)),
+    and per compute unit the fraction of the kernel's cycles its vector L1 was stalled on data
+    pending from L2 (TCP_PENDING_STALL_CYCLES, summed over the 256 units), its texture addresser
+    was stalled by the L1 (address and data paths), and per L2 channel the cycles read requests
+    waited for DRAM credits (summed over 8 XCDs x 16 channels).  GRBM_GUI_ACTIVE is summed over
+    the 8 XCDs."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    print(f"# rocprofv3 memory-side counters per dispatch: {workload_name(config)}")
+    print(f"command: {command}")
+    print(f"source_hash: {kernel_source_hash(SOURCE_DIR)}")
+    print("# l2_hit = TCC_HIT / (TCC_HIT + TCC_MISS); l1_pending, ta_addr, ta_data = TCP_PENDING_STALL_CYCLES, "
+          "TA_ADDR/DATA_STALLED_BY_TC_CYCLES over (256 CUs x GRBM_GUI_ACTIVE / 8); dram_credit = "
+          "TCC_EA0_RDREQ_DRAM_CREDIT_STALL over (128 channels x GRBM_GUI_ACTIVE / 8); medians over dispatches")
+    print(f"{'stage':<12} {'l2_hit':>7} {'l1_pending':>10} {'ta_addr':>8} {'ta_data':>8} {'dram_credit':>11}  kernel")
+    med = lambda v: sorted(v)[len(v) // 2]
+    for name, c in sorted(acc.items()):
+        st = _stage_of(name, config)
+        if st is None or not st.startswith("gemm") or not all(k in c for k in MEMORY_COUNTERS):
+            continue
+        cyc = med(c["GRBM_GUI_ACTIVE"]) / 8.0
+        hit, miss = med(c["TCC_HIT_sum"]), med(c["TCC_MISS_sum"])
+        print(f"{st:<12} {hit / (hit + miss):>7.3f} {med(c['TCP_PENDING_STALL_CYCLES_sum']) / (256 * cyc):>10.3f} "
+              f"{med(c['TA_ADDR_STALLED_BY_TC_CYCLES_sum']) / (256 * cyc):>8.3f} "
+              f"{med(c['TA_DATA_STALLED_BY_TC_CYCLES_sum']) / (256 * cyc):>8.3f} "
+              f"{med(c['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum']) / (128 * cyc):>11.4f}  "
+              f"{name.split('(')[0].replace('void ', '')}")
+
+
 # ------------------------------------------------------------------ benchmark
 def main():
     ap = argparse.ArgumentParser()
@@ -363,6 +400,7 @@ def main():
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-mfma", metavar="DIR")
+    ap.add_argument("--summarize-memory", metavar="DIR")
     ap.add_argument("--command", default="", help="profiler command recorded in a summary")
     ap.add_argument("--source-dir", default=None, help="kernel sources the profiled run used (for the hash)")
     args = ap.parse_args()
@@ -374,6 +412,8 @@ def main():
         return summarize_stats(args.summarize_stats, run_name, args.command)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters, run_name, args.command)
+    if args.summarize_memory:
+        return summarize_memory(args.summarize_memory, run_name, args.command)
     if args.summarize_mfma:
         return summarize_mfma(args.summarize_mfma, run_name, args.command)
     if args.gpus != 1:
