@@ -19,7 +19,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_H
 
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_saved_bytes", "moe_route", "moe_route_noalloc", "moe_plan",
                 "moe_forward", "moe_forward_fused", "moe_backward", "moe_router_logits", "moe_router_backward",
-                "moe_permute", "moe_combine", "moe_mxfp8_quantize", "moe_set_stage_hook", "moe_status_string")
+                "moe_permute", "moe_combine", "moe_mxfp8_quantize", "moe_mxfp8_quantize_weights", "moe_set_stage_hook",
+                "moe_status_string")
 
 
 class MoeDims(ctypes.Structure):
@@ -67,6 +68,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_permute.argtypes = [dp, vp, vp, vp, vp]
     lib.moe_combine.argtypes = [dp, vp, vp, vp, vp]
     lib.moe_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, i32, vp, vp, vp]
+    lib.moe_mxfp8_quantize_weights.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [vp] * 5
     lib.moe_set_stage_hook.argtypes = [STAGE_HOOK, vp]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -189,6 +191,12 @@ def moe_mxfp8_quantize(src, batch, rows, cols, block_axis, codes, exps, stream=N
                                                                    _ptr(codes), _ptr(exps), _stream(stream)))
 
 
+def moe_mxfp8_quantize_weights(src, batch, rows, cols, col_codes, col_exps, row_codes, row_words, stream=None):
+    _check("moe_mxfp8_quantize_weights",
+           load_library().moe_mxfp8_quantize_weights(_ptr(src), batch, rows, cols, _ptr(col_codes), _ptr(col_exps),
+                                                     _ptr(row_codes), _ptr(row_words), _stream(stream)))
+
+
 _hook_ref = None
 
 
@@ -244,7 +252,8 @@ __all__ = ["MoeDims", "MoEError", "dims", "load_library", "status_string", "moe_
            "moe_route", "moe_route_noalloc", "moe_plan", "moe_forward", "moe_forward_fused", "moe_backward",
            "moe_router_logits",
            "moe_router_backward", "moe_permute", "moe_combine",
-           "moe_mxfp8_quantize", "moe_set_stage_hook", "alloc_layer_buffers", "ENTRY_POINTS", "MOE_BF16",
+           "moe_mxfp8_quantize", "moe_mxfp8_quantize_weights", "moe_set_stage_hook", "alloc_layer_buffers",
+           "ENTRY_POINTS", "MOE_BF16",
            "MOE_FP8_E4M3", "MOE_MXFP8", "MOE_WS_ROUTE", "MOE_WS_FORWARD",
            "MOE_WS_BACKWARD", "MOE_WS_ROUTER", "MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_WORKSPACE",
            "MOE_ERR_HIP", "MOE_ERR_ALIGN"]

@@ -644,10 +644,17 @@ int moe_combine(const moe_dims* dims, const void* op, const int32_t* inv_perm, v
   return MOE_OK;
 }
 
+// batch x rows x cols below 2^40 elements, each side within int range (checked without overflow)
+static bool mx_size_ok(int64_t batch, int64_t rows, int64_t cols) {
+  if (batch < 0 || rows < 0 || cols < 0 || rows > (1 << 30) || cols > (1 << 30)) return false;
+  if (rows == 0 || cols == 0) return true;
+  return batch <= (((int64_t)1 << 40) - 1) / (rows * cols);  // rows * cols <= 2^60: no overflow
+}
+
 int moe_mxfp8_quantize(const void* src, int64_t batch, int64_t rows, int64_t cols, int block_axis, void* codes,
                        void* exps, void* stream) {
-  if (batch < 0 || rows < 0 || cols < 0 || (block_axis != 0 && block_axis != 1)) return MOE_ERR_SHAPE;
-  if (rows > (1 << 30) || cols > (1 << 30) || batch * rows * cols >= ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  if (block_axis != 0 && block_axis != 1) return MOE_ERR_SHAPE;
+  if (!mx_size_ok(batch, rows, cols)) return MOE_ERR_SHAPE;
   if (block_axis == 1 ? (cols % 32 != 0) : (rows % 32 != 0 || cols % 8 != 0)) return MOE_ERR_SHAPE;
   if (batch * rows * cols == 0) return MOE_OK;
   if (!src || !codes || !exps) return MOE_ERR_NULL;
@@ -655,6 +662,20 @@ int moe_mxfp8_quantize(const void* src, int64_t batch, int64_t rows, int64_t col
   hipStream_t st = (hipStream_t)stream;
   MOE_TRY("mx_quant", launch_mx_quant((const uint16_t*)src, batch, (int)rows, (int)cols, block_axis == 0 ? 1 : 0,
                                       (uint8_t*)codes, (uint8_t*)exps, st));
+  return MOE_OK;
+}
+
+int moe_mxfp8_quantize_weights(const void* src, int64_t batch, int64_t rows, int64_t cols, void* col_codes,
+                               void* col_exps, void* row_codes, void* row_words, void* stream) {
+  if (!mx_size_ok(batch, rows, cols)) return MOE_ERR_SHAPE;
+  if (rows % 32 != 0 || cols % 256 != 0) return MOE_ERR_SHAPE;
+  if (batch * rows * cols == 0) return MOE_OK;
+  if (!src || !col_codes || !col_exps || !row_codes || !row_words) return MOE_ERR_NULL;
+  if (!al16(src) || !al16(col_codes) || !al16(row_codes) || ((uintptr_t)col_exps & 7u) || ((uintptr_t)row_words & 3u))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  MOE_TRY("mx_quant", launch_mx_quant_dual((const uint16_t*)src, batch, (int)rows, (int)cols, (uint8_t*)col_codes,
+                                           (uint8_t*)col_exps, (uint8_t*)row_codes, (uint8_t*)row_words, st));
   return MOE_OK;
 }
 

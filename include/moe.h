@@ -235,6 +235,19 @@ int moe_set_stage_hook(moe_stage_hook hook, void* user);
 int moe_mxfp8_quantize(const void* src, int64_t batch, int64_t rows, int64_t cols, int block_axis, void* codes,
                        void* exps, void* stream);
 
+/* The MOE_MXFP8 path's weight quantiser on its own: one read of bf16 src [batch, rows, cols]
+ * (row-major; rows % 32 == 0, cols % 256 == 0) writes both orientations of each matrix.
+ * col_codes / col_exps: blocks of 32 consecutive rows of one column, exponents [batch, rows/32,
+ * cols] (as block_axis = 0 above).  row_codes / row_words: blocks of 32 consecutive values of a
+ * row, with the exponents as 32-bit words by 128-column step, [batch, cols/128, rows] words:
+ * word (t, r) holds the E8M0 bytes of blocks 4t .. 4t+3 of row r (byte j for block 4t + j), the
+ * layout the MXFP8 GEMMs read.  Codes have src's shape.  src and the codes 16-byte aligned,
+ * col_exps 8-byte aligned, row_words 4-byte aligned.  ([JAX] "Csoportosított mátrixszorzás és
+ * összevont adatmozgatás": MXFP8 blocks along each product's K; a weight matrix is the K operand
+ * of the forward along its rows and of the data gradient along its columns.) */
+int moe_mxfp8_quantize_weights(const void* src, int64_t batch, int64_t rows, int64_t cols, void* col_codes,
+                               void* col_exps, void* row_codes, void* row_words, void* stream);
+
 /* Static string for a status code (for MOE_ERR_HIP: the last HIP error on this thread). */
 const char* moe_status_string(int status);
 

@@ -191,6 +191,16 @@ def test_mxfp8_argument_rules(lib):
     assert q(None, 1, 64, 64, 1, F, F) == moe.MOE_ERR_NULL
     assert q(F, 1, 64, 64, 1, F + 8, F) == moe.MOE_ERR_ALIGN
     assert q(F, 0, 64, 64, 1, None, None) == moe.MOE_OK         # empty input: nothing to do
+    assert q(F, 1 << 20, 1 << 12, 1 << 12, 1, F, F) == moe.MOE_ERR_SHAPE   # 2^44 elements
+    w = lambda *a: lib.moe_mxfp8_quantize_weights(*a, None)
+    assert w(F, 1, 64, 384, F, F, F, F) == moe.MOE_ERR_SHAPE    # cols % 256 == 0
+    assert w(F, 1, 48, 256, F, F, F, F) == moe.MOE_ERR_SHAPE    # rows % 32 == 0
+    assert w(F, -1, 64, 256, F, F, F, F) == moe.MOE_ERR_SHAPE
+    assert w(F, 1 << 20, 1 << 12, 1 << 12, F, F, F, F) == moe.MOE_ERR_SHAPE
+    assert w(F, 1, 64, 256, F, None, F, F) == moe.MOE_ERR_NULL
+    assert w(F, 1, 64, 256, F, F + 4, F, F) == moe.MOE_ERR_ALIGN   # column exponents: 8-byte aligned
+    assert w(F, 1, 64, 256, F, F, F, F + 2) == moe.MOE_ERR_ALIGN   # row exponent words: 4-byte aligned
+    assert w(F, 0, 64, 256, None, None, None, None) == moe.MOE_OK
 
 
 def test_mxfp8_padded_rows_rule(lib):

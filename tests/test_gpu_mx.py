@@ -36,6 +36,33 @@ def test_mx_quantize_bitexact(shape, axis):
     np.testing.assert_array_equal(_values(codes.cpu().numpy()), _values(rc))
 
 
+@pytest.mark.parametrize("shape", [(2, 64, 512), (1, 96, 256), (3, 32, 768)])
+def test_mx_weight_quantizer_bitexact(shape):
+    """The layer's weight quantiser (both orientations from one read) against the oracle's MX
+    quantiser along each axis; the row-block exponents come as words by 128-column step."""
+    g = np.random.default_rng(sum(shape) + 7)
+    v = (g.normal(0, 1, shape) * np.exp2(g.integers(-8, 8, shape[:1] + (1, 1)))).astype(np.float32)
+    v[:, :32, :8] = 0.0                                       # all-zero blocks in both orientations
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)
+    src = bf16_dev(bits)
+    B, R, C = shape
+    cc = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    ce = torch.empty((B, R // 32, C), dtype=torch.uint8, device="cuda")
+    rcodes = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    rw = torch.empty((B, C // 128, R, 4), dtype=torch.uint8, device="cuda")
+    print(f"[case] mx weight quantiser {shape}", flush=True)
+    moe.moe_mxfp8_quantize_weights(src, B, R, C, cc, ce, rcodes, rw)
+    torch.cuda.synchronize()
+    x = oracle.bf16_to_f64(bits)
+    oc, oe = oracle.mx_quantize(x, axis=1)                   # blocks of 32 rows of a column
+    np.testing.assert_array_equal(ce.cpu().numpy(), oe)
+    np.testing.assert_array_equal(_values(cc.cpu().numpy()), _values(oc))
+    orc, ore = oracle.mx_quantize(x, axis=2)                 # blocks of 32 values of a row
+    words = rw.cpu().numpy()                                 # [B, C/128, R, 4]: byte j = block 4t + j
+    np.testing.assert_array_equal(words.transpose(0, 2, 1, 3).reshape(B, R, C // 32), ore)
+    np.testing.assert_array_equal(_values(rcodes.cpu().numpy()), _values(orc))
+
+
 def _mx_oracle(inp):
     """fp64 layer on the MX-quantised operands, with the same quantisation points as the GPU
     path except the intermediates (As, dH), which the oracle keeps exact."""
