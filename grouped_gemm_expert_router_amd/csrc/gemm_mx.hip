@@ -559,8 +559,101 @@ __global__ __launch_bounds__(256) void mx_quant_dual_kernel(const uint16_t* __re
   }
 }
 
+// The same for cols % 512 == 0 with 32 x 512 tiles: thread t owns 4 rows (group t / 32) x 16
+// columns (chunk t % 32), so every code store is 16 bytes.  Row blocks: 2 neighbouring lanes.
+// Column blocks: the 8 row groups' maxima meet in LDS; thread t reduces columns 2t and 2t+1.
+__global__ __launch_bounds__(256) void mx_quant_dual16_kernel(const uint16_t* __restrict__ src, int rows, int cols,
+                                                              uint8_t* __restrict__ qc, uint8_t* __restrict__ qce,
+                                                              uint8_t* __restrict__ qr, uint8_t* __restrict__ qre) {
+  __shared__ float s_amax[8][512];
+  __shared__ int s_cex[512];         // column-block exponents s of the tile's 512 columns
+  __shared__ uint8_t s_rex[32][16];  // row-block exponent bytes: [row][block]
+  const int t = threadIdx.x, cc = t & 31, rg = t >> 5;
+  const int tiles_c = cols / 512, tiles_r = rows / 32;
+  const int64_t b = blockIdx.x / (tiles_r * tiles_c);
+  const int rem = blockIdx.x % (tiles_r * tiles_c);
+  const int r0 = (rem / tiles_c) * 32, tc = rem % tiles_c, c0 = tc * 512 + cc * 16;
+  const int64_t mat = b * (int64_t)rows * cols;
+  float v[4][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t* p = src + mat + (int64_t)(r0 + 4 * rg + i) * cols + c0;
+    const uint4 w0 = *(const uint4*)p, w1 = *(const uint4*)(p + 8);
+    const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      v[i][2 * q] = lo_bf16(w[q]);
+      v[i][2 * q + 1] = hi_bf16(w[q]);
+    }
+  }
+  // row blocks: 32 columns = lanes cc and cc ^ 1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) m = fmaxf(m, fabsf(v[i][c]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    const int sx = mx_exponent(m);
+    const float inv = ldexpf(1.0f, -sx);  // exact: a power of two
+    uint4 o;
+    o.x = pack_e4m3x4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+    o.y = pack_e4m3x4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
+    o.z = pack_e4m3x4(v[i][8] * inv, v[i][9] * inv, v[i][10] * inv, v[i][11] * inv);
+    o.w = pack_e4m3x4(v[i][12] * inv, v[i][13] * inv, v[i][14] * inv, v[i][15] * inv);
+    *(uint4*)(qr + mat + (int64_t)(r0 + 4 * rg + i) * cols + c0) = o;
+    if ((cc & 1) == 0) s_rex[4 * rg + i][cc >> 1] = (uint8_t)(sx + 127);
+  }
+  // column blocks: this thread's maxima over its 4 rows, then over the 8 row groups
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(v[i][c]));
+    s_amax[rg][cc * 16 + c] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = 2 * t + h;
+    float m = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) m = fmaxf(m, s_amax[g][col]);
+    s_cex[col] = mx_exponent(m);
+  }
+  if (t < 128) {  // row-block exponent words: 4 k steps of 128 columns x 32 rows
+    const int h = t >> 5, r = t & 31;
+    const int64_t kstep = (int64_t)tc * 4 + h;
+    *(uint32_t*)(qre + ((b * (cols / 128) + kstep) * rows + r0 + r) * 4) = *(const uint32_t*)&s_rex[r][4 * h];
+  }
+  __syncthreads();
+  float inv[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) inv[c] = ldexpf(1.0f, -s_cex[cc * 16 + c]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 o;
+    o.x = pack_e4m3x4(v[i][0] * inv[0], v[i][1] * inv[1], v[i][2] * inv[2], v[i][3] * inv[3]);
+    o.y = pack_e4m3x4(v[i][4] * inv[4], v[i][5] * inv[5], v[i][6] * inv[6], v[i][7] * inv[7]);
+    o.z = pack_e4m3x4(v[i][8] * inv[8], v[i][9] * inv[9], v[i][10] * inv[10], v[i][11] * inv[11]);
+    o.w = pack_e4m3x4(v[i][12] * inv[12], v[i][13] * inv[13], v[i][14] * inv[14], v[i][15] * inv[15]);
+    *(uint4*)(qc + mat + (int64_t)(r0 + 4 * rg + i) * cols + c0) = o;
+  }
+  if (t < 128) {  // column-block exponents: 4 bytes per thread
+    uint32_t ev = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ev |= (uint32_t)(s_cex[4 * t + j] + 127) << (8 * j);
+    *(uint32_t*)(qce + (b * (rows / 32) + r0 / 32) * (int64_t)cols + tc * 512 + 4 * t) = ev;
+  }
+}
+
 hipError_t launch_mx_quant_dual(const uint16_t* src, int64_t batch, int rows, int cols, uint8_t* qc, uint8_t* qce,
                                 uint8_t* qr, uint8_t* qre, hipStream_t st) {
+  if (cols % 512 == 0) {
+    const int64_t blocks = batch * (rows / 32) * (cols / 512);
+    if (blocks == 0) return hipSuccess;
+    mx_quant_dual16_kernel<<<(unsigned)blocks, 256, 0, st>>>(src, rows, cols, qc, qce, qr, qre);
+    return hipGetLastError();
+  }
   const int64_t blocks = batch * (rows / 32) * (cols / 256);
   if (blocks == 0) return hipSuccess;
   mx_quant_dual_kernel<<<(unsigned)blocks, 256, 0, st>>>(src, rows, cols, qc, qce, qr, qre);

@@ -36,7 +36,7 @@ def test_mx_quantize_bitexact(shape, axis):
     np.testing.assert_array_equal(_values(codes.cpu().numpy()), _values(rc))
 
 
-@pytest.mark.parametrize("shape", [(2, 64, 512), (1, 96, 256), (3, 32, 768)])
+@pytest.mark.parametrize("shape", [(2, 64, 512), (2, 64, 1536), (1, 96, 256), (3, 32, 768)])
 def test_mx_weight_quantizer_bitexact(shape):
     """The layer's weight quantiser (both orientations from one read) against the oracle's MX
     quantiser along each axis; the row-block exponents come as words by 128-column step."""
