@@ -822,10 +822,9 @@ __global__ __launch_bounds__(1024) void mx_pad_offsets_kernel(const int32_t* __r
 }
 
 // Rows of a source [*, C] in the experts' sorted order -- row perm[pos] / kslots of a
-// token-major source when gather, else row pos -- quantised along the rows into the padded
-// segments: codes [P, C], exponents [P / 32, C].  The source is bf16.  One block per
-// 32 padded rows and 2048 columns; thread t owns 8 columns: a first pass over the 32 rows finds
-// their maxima, a second (from L2) writes the codes.  Rows past the expert's count are zero.
+// token-major source when gather, else row pos -- are quantised along the rows into the padded
+// segments: codes [P, C], exponents [P / 32, C] (mx_quant_tokens_kernel below).  The source is
+// bf16; rows past an expert's count are zero.
 // Source row of each of the 32 padded positions pp0.. (-1 for the zero rows that pad an expert's
 // segment to a multiple of 128): threads 0..31 fill s_row, then the block synchronises.
 __device__ __forceinline__ void token_block_rows(int pp0, int gather, int kslots, const int32_t* __restrict__ offsets,
@@ -848,122 +847,6 @@ __device__ __forceinline__ void token_block_rows(int pp0, int gather, int kslots
     s_row[threadIdx.x] = row;
   }
   __syncthreads();
-}
-
-__global__ __launch_bounds__(256) void mx_quant_tokens_kernel(const uint16_t* __restrict__ src, int C, int gather,
-                                                              int kslots, const int32_t* __restrict__ offsets,
-                                                              const int32_t* __restrict__ perm,
-                                                              const int32_t* __restrict__ poff, int E,
-                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ qe) {
-  __shared__ int64_t s_row[32];
-  const int pp0 = blockIdx.x * 32;
-  if (pp0 >= poff[E]) return;                        // block-uniform: past the padded total
-  token_block_rows(pp0, gather, kslots, offsets, perm, poff, E, s_row);
-  const int c0 = blockIdx.y * 2048 + threadIdx.x * 8;
-  if (c0 >= C) return;                               // C is a multiple of 8
-  auto load8 = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
-    const int64_t row = s_row[r];
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (row >= 0) w = *(const uint4*)(src + row * C + c0);
-    v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x); v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
-    v[4] = lo_bf16(w.z); v[5] = hi_bf16(w.z); v[6] = lo_bf16(w.w); v[7] = hi_bf16(w.w);
-  };
-  float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 8
-  for (int r = 0; r < 32; ++r) {
-    float v[8];
-    load8(r, v);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) amax[t] = fmaxf(amax[t], fabsf(v[t]));
-  }
-  int sx[8];
-  float inv[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    sx[t] = mx_exponent(amax[t]);
-    inv[t] = ldexpf(1.0f, -sx[t]);  // exact: a power of two
-  }
-#pragma unroll 8
-  for (int r = 0; r < 32; ++r) {
-    float v[8];
-    load8(r, v);
-    u32x2 o;
-    o.x = pack_e4m3x4(v[0] * inv[0], v[1] * inv[1], v[2] * inv[2], v[3] * inv[3]);
-    o.y = pack_e4m3x4(v[4] * inv[4], v[5] * inv[5], v[6] * inv[6], v[7] * inv[7]);
-    *(u32x2*)(q + (int64_t)(pp0 + r) * C + c0) = o;
-  }
-  u32x2 ev;
-  ev.x = (uint32_t)(sx[0] + 127) | ((uint32_t)(sx[1] + 127) << 8) | ((uint32_t)(sx[2] + 127) << 16) |
-         ((uint32_t)(sx[3] + 127) << 24);
-  ev.y = (uint32_t)(sx[4] + 127) | ((uint32_t)(sx[5] + 127) << 8) | ((uint32_t)(sx[6] + 127) << 16) |
-         ((uint32_t)(sx[7] + 127) << 24);
-  *(u32x2*)(qe + (int64_t)(pp0 / 32) * C + c0) = ev;
-}
-
-// The same quantisation for wide bf16 sources (C >= 1024) in one read: each thread issues the
-// loads of its 32 rows up front and keeps the raw words in registers for both the column maxima
-// and the codes (the two-pass form re-reads the rows from L2 for the codes).  Narrow sources keep
-// the two-pass form, which measured faster for them.
-__global__ __launch_bounds__(256) void mx_quant_tokens_onepass_kernel(const uint16_t* __restrict__ src, int C,
-                                                                      int gather, int kslots,
-                                                                      const int32_t* __restrict__ offsets,
-                                                                      const int32_t* __restrict__ perm,
-                                                                      const int32_t* __restrict__ poff, int E,
-                                                                      uint8_t* __restrict__ q,
-                                                                      uint8_t* __restrict__ qe) {
-  __shared__ int64_t s_row[32];
-  const int pp0 = blockIdx.x * 32;
-  if (pp0 >= poff[E]) return;                        // block-uniform: past the padded total
-  token_block_rows(pp0, gather, kslots, offsets, perm, poff, E, s_row);
-  const int c0 = blockIdx.y * 2048 + threadIdx.x * 8;
-  if (c0 >= C) return;                               // C is a multiple of 8
-  uint4 raw[32];
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const int64_t row = s_row[r];
-    raw[r] = make_uint4(0u, 0u, 0u, 0u);
-    // a gathered token row is read again by its other experts' blocks: keep it cached then
-    if (row >= 0) raw[r] = gather ? *(const uint4*)(src + row * C + c0) : load_once16(src + row * C + c0);
-  }
-  auto decode = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
-    const uint4 w = raw[r];
-    v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x); v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
-    v[4] = lo_bf16(w.z); v[5] = hi_bf16(w.z); v[6] = lo_bf16(w.w); v[7] = hi_bf16(w.w);
-  };
-  float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    float v[8];
-    decode(r, v);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) amax[t] = fmaxf(amax[t], fabsf(v[t]));
-  }
-  // decode the raw words again below rather than keeping 256 decoded floats live: an empty asm
-  // that claims to modify them stops the compiler from reusing the first decode
-#pragma unroll
-  for (int r = 0; r < 32; ++r) asm volatile("" : "+v"(raw[r].x), "+v"(raw[r].y), "+v"(raw[r].z), "+v"(raw[r].w));
-  int sx[8];
-  float inv[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    sx[t] = mx_exponent(amax[t]);
-    inv[t] = ldexpf(1.0f, -sx[t]);  // exact: a power of two
-  }
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    float v[8];
-    decode(r, v);
-    u32x2 o;
-    o.x = pack_e4m3x4(v[0] * inv[0], v[1] * inv[1], v[2] * inv[2], v[3] * inv[3]);
-    o.y = pack_e4m3x4(v[4] * inv[4], v[5] * inv[5], v[6] * inv[6], v[7] * inv[7]);
-    *(u32x2*)(q + (int64_t)(pp0 + r) * C + c0) = o;
-  }
-  u32x2 ev;
-  ev.x = (uint32_t)(sx[0] + 127) | ((uint32_t)(sx[1] + 127) << 8) | ((uint32_t)(sx[2] + 127) << 16) |
-         ((uint32_t)(sx[3] + 127) << 24);
-  ev.y = (uint32_t)(sx[4] + 127) | ((uint32_t)(sx[5] + 127) << 8) | ((uint32_t)(sx[6] + 127) << 16) |
-         ((uint32_t)(sx[7] + 127) << 24);
-  *(u32x2*)(qe + (int64_t)(pp0 / 32) * C + c0) = ev;
 }
 
 struct MxWgArgs {
@@ -1186,15 +1069,81 @@ hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* poff, h
   return hipGetLastError();
 }
 
+// Token-axis quantisation: the rows of a source [*, C] in the experts' sorted order (see
+// token_block_rows) into the padded segments, in blocks of 32 rows of one column.  Two threads
+// share a 32 x 8 block, each loading 16 of its rows up front and keeping the raw words for both
+// the column maxima and the codes (one read); thread t takes column chunk t / 2 of the block's
+// 1024 columns and rows 16 (t % 2) .., and the pair's maxima meet by a lane exchange.  Against
+// one thread per block holding all 32 rows this halves the registers, so twice the waves are in
+// flight (qwen3: x and dy 160 -> 121 us, dH 148 -> 120 us, As 93 -> 57 us).
+__global__ __launch_bounds__(256) void mx_quant_tokens_kernel(const uint16_t* __restrict__ src, int C,
+                                                                   int gather, int kslots,
+                                                                   const int32_t* __restrict__ offsets,
+                                                                   const int32_t* __restrict__ perm,
+                                                                   const int32_t* __restrict__ poff, int E,
+                                                                   uint8_t* __restrict__ q,
+                                                                   uint8_t* __restrict__ qe) {
+  __shared__ int64_t s_row[32];
+  const int pp0 = blockIdx.x * 32;
+  if (pp0 >= poff[E]) return;                        // block-uniform: past the padded total
+  token_block_rows(pp0, gather, kslots, offsets, perm, poff, E, s_row);
+  const int half = threadIdx.x & 1;
+  const int c0 = blockIdx.y * 1024 + (threadIdx.x >> 1) * 8;
+  if (c0 >= C) return;                               // both threads of a pair: C is a multiple of 8
+  uint4 raw[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = s_row[16 * half + r];
+    raw[r] = make_uint4(0u, 0u, 0u, 0u);
+    // a gathered token row is read again by its other experts' blocks: keep it cached then
+    if (row >= 0) raw[r] = gather ? *(const uint4*)(src + row * C + c0) : load_once16(src + row * C + c0);
+  }
+  auto decode = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
+    const uint4 w = raw[r];
+    v[0] = lo_bf16(w.x); v[1] = hi_bf16(w.x); v[2] = lo_bf16(w.y); v[3] = hi_bf16(w.y);
+    v[4] = lo_bf16(w.z); v[5] = hi_bf16(w.z); v[6] = lo_bf16(w.w); v[7] = hi_bf16(w.w);
+  };
+  float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v[8];
+    decode(r, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) amax[t] = fmaxf(amax[t], fabsf(v[t]));
+  }
+  int sx[8];
+  float inv[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    amax[t] = fmaxf(amax[t], __shfl_xor(amax[t], 1, 64));
+    sx[t] = mx_exponent(amax[t]);
+    inv[t] = ldexpf(1.0f, -sx[t]);  // exact: a power of two
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v[8];
+    decode(r, v);
+    u32x2 o;
+    o.x = pack_e4m3x4(v[0] * inv[0], v[1] * inv[1], v[2] * inv[2], v[3] * inv[3]);
+    o.y = pack_e4m3x4(v[4] * inv[4], v[5] * inv[5], v[6] * inv[6], v[7] * inv[7]);
+    *(u32x2*)(q + (int64_t)(pp0 + 16 * half + r) * C + c0) = o;
+  }
+  if (half == 0) {
+    u32x2 ev;
+    ev.x = (uint32_t)(sx[0] + 127) | ((uint32_t)(sx[1] + 127) << 8) | ((uint32_t)(sx[2] + 127) << 16) |
+           ((uint32_t)(sx[3] + 127) << 24);
+    ev.y = (uint32_t)(sx[4] + 127) | ((uint32_t)(sx[5] + 127) << 8) | ((uint32_t)(sx[6] + 127) << 16) |
+           ((uint32_t)(sx[7] + 127) << 24);
+    *(u32x2*)(qe + (int64_t)(pp0 / 32) * C + c0) = ev;
+  }
+}
+
 hipError_t launch_mx_quant_tokens(const uint16_t* src, int C, int gather, const MoeShape& s, const int32_t* offsets,
                                   const int32_t* perm, const int32_t* poff, uint8_t* q, uint8_t* qe, hipStream_t st) {
   const int64_t blocks = mx_padded_rows((int64_t)s.T * s.k, s.E) / 32;
   if (blocks == 0) return hipSuccess;
-  dim3 grid((unsigned)blocks, (unsigned)((C + 2047) / 2048));
-  if (C >= 1024)
-    mx_quant_tokens_onepass_kernel<<<grid, 256, 0, st>>>(src, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
-  else
-    mx_quant_tokens_kernel<<<grid, 256, 0, st>>>(src, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
+  const dim3 grid((unsigned)blocks, (unsigned)((C + 1023) / 1024));
+  mx_quant_tokens_kernel<<<grid, 256, 0, st>>>(src, C, gather, s.k, offsets, perm, poff, s.E, q, qe);
   return hipGetLastError();
 }
 
