@@ -126,8 +126,9 @@ def stage_bytes(stage, T, d, f, E, k, A):
         return T * d * 2 + A * d + A * d // 32
     if stage in ("ksort_x", "ksort_dy"):    # token-major words (d/32 bytes a row) in, sorted by k step out
         return T * d // 32 + A * 4 + A * d // 32
-    if stage in ("mx_quant_w1", "mx_quant_w2"):
-        return E * d * f * (2 + 1) + E * d * f // 32     # one of W1 (2df) / W2 (df): bytes of W1 halved
+    if stage in ("mx_quant_w1", "mx_quant_w2"):   # bf16 in, both orientations' codes and exponents out
+        n = E * d * f * (2 if stage == "mx_quant_w1" else 1)
+        return n * 2 + 2 * n + 2 * (n // 32)
     return None
 
 
